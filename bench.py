@@ -1,0 +1,176 @@
+#!/usr/bin/env python3
+"""Benchmark: FP32 GEMM TFLOPS and fraction of the MI355X FP32 matrix peak.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--shape M N K]
+                    [--config C] [--table] [--no-cpu-baseline]
+
+A step is one gemm_f32 call (the whole hot path) on synthetic uniform[-1,1)
+operands already resident in HBM.  The default workload is M = N = K = 8192.
+Timing follows the pages' method: W untimed warm-ups, then K timed calls with
+a device synchronisation on both sides; HIP events around each call on the
+stream it is enqueued on give the per-launch kernel time used for the
+roofline.  ``--table`` also times the 2048^3 case and every other workload
+shape (on stderr).  The last stdout line is one JSON object.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP32 GEMM TFLOPS and % of FP32 peak at M=N=K=2048 and 8192"
+PEAK_FP32_MATRIX_TFLOPS = 157.3     # MI355X dense FP32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+TABLE = [(512, 512, 512), (1025, 1023, 1000), (1, 1, 1), (17, 33, 65), (1000, 1000, 1000),
+         (2048, 2048, 2048), (8192, 8192, 8192), (8192, 8192, 128), (16384, 64, 4096),
+         (64, 16384, 4096), (4096, 4096, 16384)]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1):
+    """Returns a dict of timings for one shape (inputs generated and copied first)."""
+    from dense_fp32_gemm_amd import inputs
+    A, B = inputs.uniform(M, N, K)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.empty((M, N), dtype=torch.float32, device=dev)
+    del A, B
+    stream = torch.cuda.current_stream()
+    s = stream.cuda_stream
+
+    def call():
+        rc = gb.gemm_f32_with_config(config, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                                     dC.data_ptr(), N, s)
+        if rc != gb.GEMM_F32_OK:
+            raise gb.GemmError(rc)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        call()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])   # ms
+    flop = 2.0 * M * N * K
+    rc, desc = gb.gemm_f32_describe(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+    out = {
+        "M": M, "N": N, "K": K, "kernel": desc,
+        "wall_ms_per_step": 1e3 * wall / steps,
+        "event_ms_mean": float(ev.mean()), "event_ms_median": float(np.median(ev)),
+        "event_ms_min": float(ev.min()),
+        "tflops_wall": flop / (wall / steps) / 1e12,
+        "tflops_event_mean": flop / (ev.mean() * 1e-3) / 1e12,
+        "algorithmic_bytes": 4.0 * (M * K + K * N + M * N),
+    }
+    out["gbs_event_mean"] = out["algorithmic_bytes"] / (ev.mean() * 1e-3) / 1e9
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(M, N, K, budget_s=12.0):
+    """The oracle on a bounded row block of the same problem, scaled to TFLOPS."""
+    import oracle
+    from dense_fp32_gemm_amd import inputs
+    A, B = inputs.uniform(M, N, K)
+    rows = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(np.ascontiguousarray(A[:rows]), B)
+        dt = time.perf_counter() - t0
+        if dt > budget_s / 4 or rows >= M:
+            break
+        rows = min(M, int(rows * max(2.0, budget_s / 2 / max(dt, 1e-3))))
+    return {
+        "value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOPS",
+        "cores": oracle.threads(), "kind": "oracle",
+        "sample": f"first {rows} of {M} rows of C ({M}x{N}x{K} uniform operands), "
+                  f"{dt:.1f} s, binary64 accumulation, OpenMP over rows",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--shape", type=int, nargs=3, default=(8192, 8192, 8192))
+    ap.add_argument("--config", type=int, default=-1)
+    ap.add_argument("--table", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "this GEMM runs on a single MI355X and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dense_fp32_gemm_amd import binding as gb
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    gb.load()
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    M, N, K = args.shape
+    head = time_gemm(torch, gb, M, N, K, args.steps, args.warmup, args.config)
+    log(json.dumps(head))
+    extra = {}
+    if args.table:
+        for shp in TABLE:
+            if tuple(shp) == (M, N, K):
+                continue
+            r = time_gemm(torch, gb, *shp, args.steps, args.warmup, args.config)
+            extra["x".join(map(str, shp))] = round(r["tflops_event_mean"], 3)
+            log(f"{r['M']:>6} {r['N']:>6} {r['K']:>6}  {r['event_ms_mean']*1e3:10.1f} us  "
+                f"{r['tflops_event_mean']:8.2f} TFLOPS  {r['gbs_event_mean']:8.1f} GB/s  {r['kernel']}")
+
+    achieved = head["tflops_event_mean"]
+    line = {
+        "metric": METRIC,
+        "value": round(head["tflops_wall"], 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["wall_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"sgemm_{M}x{N}x{K}_uniform", "M": M, "N": N, "K": K,
+                   "kernel": head["kernel"],
+                   "pct_of_fp32_matrix_peak": round(100.0 * head["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                     "peak": PEAK_FP32_MATRIX_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4), "traffic": None},
+    }
+    if extra:
+        line["config"]["other_tflops"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(M, N, K)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

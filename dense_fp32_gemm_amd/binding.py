@@ -1,0 +1,127 @@
+"""ctypes binding of libgemm_f32.so (include/gemm_f32.h), same names.
+
+Argument marshalling only: every step of the product runs in the library's
+HIP kernels.  ``matmul`` is a convenience over ``gemm_f32`` that takes torch
+tensors for device memory and the current torch stream; it validates layout
+and raises on any non-zero status.  There is no fallback: if the library is
+missing and cannot be built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libgemm_f32.so")
+
+GEMM_F32_OK = 0
+GEMM_F32_ERR_DIM = 1
+GEMM_F32_ERR_LD = 2
+GEMM_F32_ERR_NULL = 3
+GEMM_F32_ERR_LAUNCH = 4
+GEMM_F32_ERR_CONFIG = 5
+GEMM_F32_ERR_ALIGN = 6
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, what: str = "gemm_f32"):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({gemm_f32_status_string(status)})")
+
+
+def load() -> ctypes.CDLL:
+    """The HIP library (built in-tree first if it is not there yet)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            from . import build
+            build.build()
+        lib = ctypes.CDLL(LIBRARY)
+        i, p = ctypes.c_int, ctypes.c_void_p
+        gemm_args = [i, i, i, p, i, p, i, p, i, p]
+        lib.gemm_f32.argtypes = gemm_args
+        lib.gemm_f32.restype = i
+        lib.gemm_f32_with_config.argtypes = [i] + gemm_args
+        lib.gemm_f32_with_config.restype = i
+        lib.gemm_f32_num_configs.argtypes = []
+        lib.gemm_f32_num_configs.restype = i
+        lib.gemm_f32_config_name.argtypes = [i]
+        lib.gemm_f32_config_name.restype = ctypes.c_char_p
+        lib.gemm_f32_describe.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.c_char_p, i]
+        lib.gemm_f32_describe.restype = i
+        lib.gemm_f32_status_string.argtypes = [i]
+        lib.gemm_f32_status_string.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+# --- the C ABI, one function per exported symbol ---------------------------
+def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """C := A . B on `stream`; A, B, C are device addresses (ints)."""
+    return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_with_config(config, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    return load().gemm_f32_with_config(config, M, N, K, A, lda, B, ldb, C, ldc, stream)
+
+
+def gemm_f32_num_configs() -> int:
+    return load().gemm_f32_num_configs()
+
+
+def gemm_f32_config_name(config: int) -> str:
+    return load().gemm_f32_config_name(config).decode()
+
+
+def gemm_f32_describe(M, N, K, A, lda, B, ldb, C, ldc) -> tuple[int, str]:
+    """(status, description) of what gemm_f32 would enqueue."""
+    buf = ctypes.create_string_buffer(256)
+    rc = load().gemm_f32_describe(M, N, K, A, lda, B, ldb, C, ldc, buf, len(buf))
+    return rc, buf.value.decode()
+
+
+def gemm_f32_status_string(status: int) -> str:
+    return load().gemm_f32_status_string(status).decode()
+
+
+def config_names() -> list[str]:
+    return [gemm_f32_config_name(c) for c in range(gemm_f32_num_configs())]
+
+
+# --- torch convenience -------------------------------------------------------
+def _row_major(t, rows: int, cols: int, name: str) -> int:
+    """Leading dimension of a 2-D float32 CUDA tensor with unit column stride."""
+    import torch
+    if t.dtype != torch.float32 or t.dim() != 2 or not t.is_cuda:
+        raise TypeError(f"{name} must be a 2-D float32 tensor on a GPU")
+    if tuple(t.shape) != (rows, cols):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {(rows, cols)}")
+    s0, s1 = t.stride()
+    if rows > 0 and cols > 1 and s1 != 1:
+        raise ValueError(f"{name} must have unit column stride")
+    if rows > 1 and s0 < cols:
+        raise ValueError(f"{name} rows overlap")
+    return max(s0 if rows > 1 else cols, cols, 1)
+
+
+def matmul(A, B, out=None, config: int = -1, stream=None):
+    """out = A @ B via gemm_f32 on the current (or given) torch stream."""
+    import torch
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K:
+        raise ValueError("inner dimensions differ")
+    lda = _row_major(A, M, K, "A")
+    ldb = _row_major(B, K, N, "B")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    ldc = _row_major(out, M, N, "out")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device)
+    rc = gemm_f32_with_config(config, M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+                              out.data_ptr(), ldc, stream.cuda_stream)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc)
+    return out

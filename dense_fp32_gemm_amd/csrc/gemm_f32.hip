@@ -1,0 +1,565 @@
+// Dense FP32 GEMM for AMD MI355X (gfx950 / CDNA4): kernels and the C ABI.
+//
+// C[M x N] = A[M x K] . B[K x N], row-major binary32 (the product of the
+// UIUC ECE408 Lecture 12 final-project page, project_template.cu section 2).
+//
+// Two kernel families:
+//
+//  * gemm_f32_mfma<Tile, VEC_A, VEC_B>: one workgroup per BM x BN tile of C.
+//    K is walked in BK-deep panels that are staged global -> VGPR -> LDS
+//    with two LDS buffers, so the next panel is fetched while the matrix
+//    cores work on the current one (one barrier per panel).  Each wave owns a
+//    (BM/WAVES_M) x (BN/WAVES_N) block of C held in 32 x 32 accumulators of
+//    v_mfma_f32_32x32x2_f32.  Ragged edges are zero-filled on load and
+//    masked on store, so every shape runs on this path.
+//  * gemm_f32_valu: a 64 x 64 LDS-tiled vector-FMA kernel (4 x 4 outputs per
+//    thread) for problems too small to fill a matrix-core tile.
+//
+// The pages' kernels (Lecture 5 and 12 notes, the cuda-gemm README) were
+// written for NVIDIA parts; what carries over is the structure -- output
+// tiling, K-panels in on-chip memory, register blocking, vector loads, double
+// buffering -- while the inner product runs on CDNA4 FP32 matrix cores with
+// 64-wide waves.
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "gemm_f32.h"
+
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kWaveSize = 64;
+constexpr int kXcdCount = 8;         // MI355X: 8 accelerator complex dies
+constexpr int64_t kMaxGrid = 1 << 20;  // workgroups per launch; larger jobs loop
+
+struct GemmArgs {
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int tiles_m, tiles_n;
+};
+
+// ---------------------------------------------------------------------------
+// Tile scheduling
+// ---------------------------------------------------------------------------
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
+// w mod 8), and each XCD has its own L2.  Renumber so that each XCD receives a
+// contiguous range of logical tiles; neighbouring tiles share A rows and B
+// columns, so their panels are fetched once per L2.
+__device__ inline int xcd_contiguous(int w, int total)
+{
+    const int per = total / kXcdCount;
+    const int rem = total % kXcdCount;
+    const int xcd = w % kXcdCount;
+    return xcd * per + (xcd < rem ? xcd : rem) + w / kXcdCount;
+}
+
+// Logical tile id -> (tile row, tile column), walking groups of `group` tile
+// rows column by column so that concurrently running tiles form a compact
+// block of C.
+__device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int group,
+                                   int &tm, int &tn)
+{
+    const int per_group = group * tiles_n;
+    const int first_m = (t / per_group) * group;
+    const int rows = min(tiles_m - first_m, group);
+    const int r = t % per_group;
+    tm = first_m + r % rows;
+    tn = r / rows;
+}
+
+// ---------------------------------------------------------------------------
+// Guarded loads: 4 consecutive elements of one row, +0.0 outside the matrix.
+// VEC = true needs a 16-byte aligned address and a row length that is a
+// multiple of 4, so a 4-element chunk is entirely inside or outside.
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncols)
+{
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (VEC) {
+        if (row_ok && col < ncols)
+            v = *reinterpret_cast<const f32x4 *>(p);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (row_ok && col + e < ncols)
+                v[e] = p[e];
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel
+// ---------------------------------------------------------------------------
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+struct MfmaTile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int kThreads = WAVES_M * WAVES_N * kWaveSize;
+    static constexpr int kWaveM = BM / WAVES_M;      // C rows per wave
+    static constexpr int kWaveN = BN / WAVES_N;      // C columns per wave
+    static constexpr int kFragM = kWaveM / 32;       // 32x32 accumulators down
+    static constexpr int kFragN = kWaveN / 32;       // 32x32 accumulators across
+    // LDS panels.  A is kept row-major ([m][k], k contiguous) so one 128-bit
+    // read gives a lane 4 consecutive k of its row; the +4 pad makes the 32
+    // rows read by a half-wave fall on distinct banks.  B is kept row-major
+    // ([k][n]); lanes read consecutive n, and the +8 pad puts the two
+    // half-waves (k and k+4) on different banks.
+    static constexpr int kStrideA = BK + 4;
+    static constexpr int kStrideB = BN + 8;
+    static constexpr int kLdsA = BM * kStrideA;
+    static constexpr int kLdsB = BK * kStrideB;
+    // 4-element chunks each thread moves per panel.
+    static constexpr int kChunksA = BM * BK / 4 / kThreads;
+    static constexpr int kChunksB = BK * BN / 4 / kThreads;
+    static constexpr int kGroup = 8;                 // tile rows per raster group
+
+    static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
+    static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
+    static_assert(BM * BK % (4 * kThreads) == 0 && kChunksA >= 1, "A panel split");
+    static_assert(BK * BN % (4 * kThreads) == 0 && kChunksB >= 1, "B panel split");
+    static_assert(2 * (kLdsA + kLdsB) * 4 <= 160 * 1024, "LDS budget");
+};
+
+// One v_mfma_f32_32x32x2_f32 adds, for the 32 x 32 block it accumulates,
+// sum over t in {0,1} of a(i,t) * b(t,j), where lane l supplies a(l%32, l/32)
+// and b(l/32, l%32).  Lane half h = l/32 therefore plays the role of k.  The
+// kernel pairs k = 8g + 4h + s (s = 0..3) in the s-th instruction of k-group
+// g: each lane reads its 4 A values with one 128-bit LDS read, every k of the
+// panel is used exactly once, and only the order of the sum changes.
+//
+// Accumulator layout (16 floats per lane): register r of lane l holds
+// C(8*(r/4) + 4*(l/32) + r%4, l%32) of the block.
+template <class T, bool VEC_A, bool VEC_B>
+__global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
+{
+    constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
+    constexpr int NT = T::kThreads;
+    __shared__ __attribute__((aligned(16))) float lds_a[2][T::kLdsA];
+    __shared__ __attribute__((aligned(16))) float lds_b[2][T::kLdsB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWaveSize;
+    const int wave = tid / kWaveSize;
+    const int wave_m = wave / T::WAVES_N;
+    const int wave_n = wave % T::WAVES_N;
+    const int li = lane % 32;        // row (A) / column (B) within a 32-block
+    const int lh = lane / 32;        // lane half: selects k = 8g + 4*lh + s
+
+    const int total = g.tiles_m * g.tiles_n;
+    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+        const int t = (int)gridDim.x == total ? xcd_contiguous(w, total) : w;
+        int tm, tn;
+        tile_coords(t, g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
+        const int m0 = tm * BM;
+        const int n0 = tn * BN;
+
+        // Per-thread panel coordinates (fixed over the K loop).
+        int a_row[T::kChunksA], a_col[T::kChunksA];
+        int b_row[T::kChunksB], b_col[T::kChunksB];
+#pragma unroll
+        for (int r = 0; r < T::kChunksA; ++r) {
+            const int f = tid + r * NT;
+            a_row[r] = f / (BK / 4);
+            a_col[r] = (f % (BK / 4)) * 4;
+        }
+#pragma unroll
+        for (int r = 0; r < T::kChunksB; ++r) {
+            const int f = tid + r * NT;
+            b_row[r] = f / (BN / 4);
+            b_col[r] = (f % (BN / 4)) * 4;
+        }
+
+        f32x4 stage_a[T::kChunksA];
+        f32x4 stage_b[T::kChunksB];
+        auto fetch = [&](int k0) {
+#pragma unroll
+            for (int r = 0; r < T::kChunksA; ++r) {
+                const int m = m0 + a_row[r];
+                const float *p = g.A + (int64_t)m * g.lda + (k0 + a_col[r]);
+                stage_a[r] = load_row4<VEC_A>(p, m < g.M, k0 + a_col[r], g.K);
+            }
+#pragma unroll
+            for (int r = 0; r < T::kChunksB; ++r) {
+                const int k = k0 + b_row[r];
+                const float *p = g.B + (int64_t)k * g.ldb + (n0 + b_col[r]);
+                stage_b[r] = load_row4<VEC_B>(p, k < g.K, n0 + b_col[r], g.N);
+            }
+        };
+        auto stash = [&](int buf) {
+#pragma unroll
+            for (int r = 0; r < T::kChunksA; ++r)
+                *reinterpret_cast<f32x4 *>(&lds_a[buf][a_row[r] * T::kStrideA + a_col[r]]) = stage_a[r];
+#pragma unroll
+            for (int r = 0; r < T::kChunksB; ++r)
+                *reinterpret_cast<f32x4 *>(&lds_b[buf][b_row[r] * T::kStrideB + b_col[r]]) = stage_b[r];
+        };
+
+        f32x16 acc[T::kFragM][T::kFragN];
+#pragma unroll
+        for (int i = 0; i < T::kFragM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::kFragN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.f;
+
+        const int ktiles = (g.K + BK - 1) / BK;
+        fetch(0);
+        stash(0);
+        if (ktiles > 1)
+            fetch(BK);
+        __syncthreads();
+
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int cur = kt & 1;
+            // Buffer cur^1 was last read before the previous barrier.
+            if (kt + 1 < ktiles) {
+                stash(cur ^ 1);
+                if (kt + 2 < ktiles)
+                    fetch((kt + 2) * BK);
+            }
+            const float *la = lds_a[cur] + (wave_m * T::kWaveM + li) * T::kStrideA + 4 * lh;
+            const float *lb = lds_b[cur] + (4 * lh) * T::kStrideB + wave_n * T::kWaveN + li;
+#pragma unroll
+            for (int kg = 0; kg < BK / 8; ++kg) {
+                f32x4 a[T::kFragM];
+                float b[4][T::kFragN];
+#pragma unroll
+                for (int i = 0; i < T::kFragM; ++i)
+                    a[i] = *reinterpret_cast<const f32x4 *>(la + i * 32 * T::kStrideA + 8 * kg);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int j = 0; j < T::kFragN; ++j)
+                        b[s][j] = lb[(8 * kg + s) * T::kStrideB + j * 32];
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < T::kFragM; ++i)
+#pragma unroll
+                        for (int j = 0; j < T::kFragN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+
+        // Epilogue: each store instruction writes two 128-byte row segments.
+#pragma unroll
+        for (int i = 0; i < T::kFragM; ++i) {
+#pragma unroll
+            for (int j = 0; j < T::kFragN; ++j) {
+                const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                    if (row < g.M && col < g.N)
+                        g.C[(int64_t)row * g.ldc + col] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Vector-FMA kernel: 64 x 64 tile, 256 threads, 4 x 4 outputs per thread.
+// ---------------------------------------------------------------------------
+constexpr int kValuTile = 64;
+constexpr int kValuBK = 16;
+constexpr int kValuThreads = 256;
+
+__global__ __launch_bounds__(kValuThreads) void gemm_f32_valu(GemmArgs g)
+{
+    // Both panels k-major ([k][m], [k][n]) so each thread reads its 4 rows and
+    // its 4 columns with one 128-bit LDS read each.
+    __shared__ __attribute__((aligned(16))) float sa[kValuBK][kValuTile + 4];
+    __shared__ __attribute__((aligned(16))) float sb[kValuBK][kValuTile + 4];
+
+    const int tid = threadIdx.x;
+    const int tx = tid % 16;          // output columns 4*tx .. 4*tx+3
+    const int ty = tid / 16;          // output rows    4*ty .. 4*ty+3
+    const int total = g.tiles_m * g.tiles_n;
+
+    for (int t = blockIdx.x; t < total; t += gridDim.x) {
+        const int m0 = (t / g.tiles_n) * kValuTile;
+        const int n0 = (t % g.tiles_n) * kValuTile;
+        float acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = 0.f;
+
+        for (int k0 = 0; k0 < g.K; k0 += kValuBK) {
+#pragma unroll
+            for (int q = 0; q < kValuTile * kValuBK / kValuThreads; ++q) {
+                const int e = tid + q * kValuThreads;
+                const int am = e / kValuBK, ak = e % kValuBK;      // A: along k
+                const int m = m0 + am, ka = k0 + ak;
+                sa[ak][am] = (m < g.M && ka < g.K) ? g.A[(int64_t)m * g.lda + ka] : 0.f;
+                const int bk = e / kValuTile, bn = e % kValuTile;  // B: along n
+                const int kb = k0 + bk, n = n0 + bn;
+                sb[bk][bn] = (kb < g.K && n < g.N) ? g.B[(int64_t)kb * g.ldb + n] : 0.f;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int k = 0; k < kValuBK; ++k) {
+                const f32x4 a = *reinterpret_cast<const f32x4 *>(&sa[k][4 * ty]);
+                const f32x4 b = *reinterpret_cast<const f32x4 *>(&sb[k][4 * tx]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = m0 + 4 * ty + i;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int col = n0 + 4 * tx + j;
+                if (row < g.M && col < g.N)
+                    g.C[(int64_t)row * g.ldc + col] = acc[i][j];
+            }
+        }
+    }
+}
+
+// K == 0: the sum is empty, C's window becomes +0.0.  A kernel rather than a
+// memset so the call stays a plain kernel launch (also under graph capture).
+__global__ __launch_bounds__(256) void fill_zero(float *C, int64_t ldc, int M, int N)
+{
+    const int64_t total = (int64_t)M * N;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x)
+        C[(e / N) * ldc + (e % N)] = 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// Configurations
+// ---------------------------------------------------------------------------
+using Tile256x128 = MfmaTile<256, 128, 16, 2, 2>;   // wave 128 x 64, 8 accumulators
+using Tile128x256 = MfmaTile<128, 256, 16, 2, 2>;   // wave 64 x 128
+using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;   // wave 64 x 64, 4 accumulators
+using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;     // wave 64 x 32
+using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;     // wave 32 x 64
+using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;       // wave 32 x 32, 1 accumulator
+
+enum ConfigId {
+    kCfgValu64 = 0,
+    kCfgMfma256x128,
+    kCfgMfma128x256,
+    kCfgMfma128x128,
+    kCfgMfma128x64,
+    kCfgMfma64x128,
+    kCfgMfma64x64,
+    kNumConfigs
+};
+
+struct ConfigInfo {
+    const char *name;
+    int bm, bn, threads;
+};
+
+const ConfigInfo kConfigs[kNumConfigs] = {
+    {"valu_64x64", kValuTile, kValuTile, kValuThreads},
+    {"mfma_256x128x16", 256, 128, Tile256x128::kThreads},
+    {"mfma_128x256x16", 128, 256, Tile128x256::kThreads},
+    {"mfma_128x128x16", 128, 128, Tile128x128::kThreads},
+    {"mfma_128x64x16", 128, 64, Tile128x64::kThreads},
+    {"mfma_64x128x16", 64, 128, Tile64x128::kThreads},
+    {"mfma_64x64x16", 64, 64, Tile64x64::kThreads},
+};
+
+template <class T>
+hipError_t launch_mfma(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
+{
+    if (va && vb)
+        gemm_f32_mfma<T, true, true><<<grid, T::kThreads, 0, s>>>(g);
+    else if (va)
+        gemm_f32_mfma<T, true, false><<<grid, T::kThreads, 0, s>>>(g);
+    else if (vb)
+        gemm_f32_mfma<T, false, true><<<grid, T::kThreads, 0, s>>>(g);
+    else
+        gemm_f32_mfma<T, false, false><<<grid, T::kThreads, 0, s>>>(g);
+    return hipGetLastError();
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile choice by shape.  The largest tile that still gives every compute unit
+// at least one tile (256 CUs) is preferred: bigger tiles re-read less of A
+// and B per FLOP, but too few tiles leave matrix cores idle.
+int select_config(int M, int N, int K)
+{
+    (void)K;
+    if (M < 16 || N < 16)
+        return kCfgValu64;
+    const int64_t cus = 256;
+    auto tiles = [&](int c) { return ceil_div(M, kConfigs[c].bm) * ceil_div(N, kConfigs[c].bn); };
+    if (tiles(kCfgMfma256x128) >= 2 * cus || tiles(kCfgMfma128x256) >= 2 * cus)
+        return M >= N ? kCfgMfma256x128 : kCfgMfma128x256;
+    if (tiles(kCfgMfma128x128) >= cus)
+        return kCfgMfma128x128;
+    if (M >= N && tiles(kCfgMfma128x64) >= cus)
+        return kCfgMfma128x64;
+    if (N > M && tiles(kCfgMfma64x128) >= cus)
+        return kCfgMfma64x128;
+    return kCfgMfma64x64;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Plan {
+    int config;
+    bool vec_a, vec_b;
+    int tiles_m, tiles_n;
+    int grid;
+};
+
+// Validates the arguments (sizes, leading dimensions, NULL pointers,
+// alignment, in that order) and fills `plan`; returns a GEMM_F32_* code.
+int make_plan(int config, int M, int N, int K, const float *A, int lda,
+              const float *B, int ldb, const float *C, int ldc, Plan *plan)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return GEMM_F32_ERR_DIM;
+    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+        return GEMM_F32_ERR_LD;
+    if (config < -1 || config >= kNumConfigs)
+        return GEMM_F32_ERR_CONFIG;
+    plan->config = -1;
+    plan->vec_a = plan->vec_b = false;
+    plan->tiles_m = plan->tiles_n = plan->grid = 0;
+    if (M == 0 || N == 0)
+        return GEMM_F32_OK;
+    if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr)))
+        return GEMM_F32_ERR_NULL;
+    if (((uintptr_t)C & 3u) || (K > 0 && (((uintptr_t)A & 3u) || ((uintptr_t)B & 3u))))
+        return GEMM_F32_ERR_ALIGN;
+    if (K == 0) {
+        plan->grid = (int)(ceil_div((int64_t)M * N, 256) < 4096 ? ceil_div((int64_t)M * N, 256) : 4096);
+        return GEMM_F32_OK;
+    }
+    const int c = config >= 0 ? config : select_config(M, N, K);
+    const int64_t tm = ceil_div(M, kConfigs[c].bm);
+    const int64_t tn = ceil_div(N, kConfigs[c].bn);
+    if (tm * tn > INT32_MAX)
+        return GEMM_F32_ERR_DIM;
+    plan->config = c;
+    plan->tiles_m = (int)tm;
+    plan->tiles_n = (int)tn;
+    plan->grid = (int)(tm * tn < kMaxGrid ? tm * tn : kMaxGrid);
+    plan->vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
+    plan->vec_b = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+    return GEMM_F32_OK;
+}
+
+int run(int config, int M, int N, int K, const float *A, int lda, const float *B,
+        int ldb, float *C, int ldc, hipStream_t stream)
+{
+    Plan p;
+    const int rc = make_plan(config, M, N, K, A, lda, B, ldb, C, ldc, &p);
+    if (rc != GEMM_F32_OK || p.grid == 0)
+        return rc;
+    if (K == 0) {
+        fill_zero<<<p.grid, 256, 0, stream>>>(C, ldc, M, N);
+        return hipGetLastError() == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+    }
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = C;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = ldc;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.tiles_m = p.tiles_m;
+    g.tiles_n = p.tiles_n;
+    hipError_t err = hipSuccess;
+    switch (p.config) {
+    case kCfgValu64:
+        gemm_f32_valu<<<p.grid, kValuThreads, 0, stream>>>(g);
+        err = hipGetLastError();
+        break;
+    case kCfgMfma256x128: err = launch_mfma<Tile256x128>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    case kCfgMfma128x256: err = launch_mfma<Tile128x256>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    case kCfgMfma128x128: err = launch_mfma<Tile128x128>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    case kCfgMfma128x64: err = launch_mfma<Tile128x64>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    case kCfgMfma64x128: err = launch_mfma<Tile64x128>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    case kCfgMfma64x64: err = launch_mfma<Tile64x64>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    default: return GEMM_F32_ERR_CONFIG;
+    }
+    return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+             float *C, int ldc, hipStream_t stream)
+{
+    return run(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_with_config(int config, int M, int N, int K, const float *A, int lda,
+                         const float *B, int ldb, float *C, int ldc, hipStream_t stream)
+{
+    return run(config, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+int gemm_f32_num_configs(void) { return kNumConfigs; }
+
+const char *gemm_f32_config_name(int config)
+{
+    return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : "";
+}
+
+int gemm_f32_describe(int M, int N, int K, const float *A, int lda, const float *B,
+                      int ldb, const float *C, int ldc, char *buf, int buflen)
+{
+    Plan p;
+    const int rc = make_plan(-1, M, N, K, A, lda, B, ldb, C, ldc, &p);
+    if (buf == nullptr || buflen <= 0)
+        return rc;
+    if (rc != GEMM_F32_OK)
+        snprintf(buf, (size_t)buflen, "invalid: %s", gemm_f32_status_string(rc));
+    else if (p.config < 0)
+        snprintf(buf, (size_t)buflen, "%s", p.grid ? "fill_zero" : "none");
+    else
+        snprintf(buf, (size_t)buflen, "%s tiles=%dx%d grid=%d threads=%d load_a=%s load_b=%s",
+                 kConfigs[p.config].name, p.tiles_m, p.tiles_n, p.grid,
+                 kConfigs[p.config].threads, p.vec_a ? "x4" : "x1", p.vec_b ? "x4" : "x1");
+    return rc;
+}
+
+const char *gemm_f32_status_string(int status)
+{
+    switch (status) {
+    case GEMM_F32_OK: return "ok";
+    case GEMM_F32_ERR_DIM: return "M, N or K is negative or the problem is too large to tile";
+    case GEMM_F32_ERR_LD: return "a leading dimension is smaller than its row length";
+    case GEMM_F32_ERR_NULL: return "a required pointer is NULL";
+    case GEMM_F32_ERR_LAUNCH: return "kernel launch failed";
+    case GEMM_F32_ERR_CONFIG: return "unknown kernel configuration";
+    case GEMM_F32_ERR_ALIGN: return "a pointer is not 4-byte aligned";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+/*
+ * gemm_f32.h -- dense single-precision matrix multiply on AMD MI355X (gfx950).
+ *
+ * The operation is the one the UIUC ECE408 Lecture 12 final-project page
+ * (project_template.cu, section 2, "tiledMatMulKernel") computes:
+ *
+ *     C[M x N] = A[M x K] . B[K x N]        row-major, binary32 in and out,
+ *
+ * i.e. C(i,j) = sum over k of A(i,k) * B(k,j), for any M, N, K >= 0, including
+ * sizes that are not multiples of any tile and the 1 x 1 x 1 case the page
+ * lists among its boundary runs.  As on the page there is no alpha/beta, no
+ * transpose and no column-major form: C is overwritten.  The page addresses
+ * packed operands; this interface adds the usual row-major leading dimensions:
+ *
+ *     A(i,k) = A[(size_t)i * lda + k]     lda >= max(1, K)
+ *     B(k,j) = B[(size_t)k * ldb + j]     ldb >= max(1, N)
+ *     C(i,j) = C[(size_t)i * ldc + j]     ldc >= max(1, N)
+ *
+ * Precision: products and sums are binary32 on the FP32 matrix cores
+ * (v_mfma_f32_*_f32; no reduced-precision xf32 forms) or the FP32 vector
+ * unit.  The summation order over k is the kernel's own, so on general
+ * inputs the result differs from the exactly rounded sum by ordinary binary32
+ * accumulation error; when every partial sum is representable in binary32
+ * (e.g. operands that are small multiples of 0.25) the result is exact.
+ *
+ * Memory and ownership: A, B and C are DEVICE pointers owned by the caller,
+ * 4-byte aligned (16-byte alignment of the base and of lda/ldb/ldc*4 lets the
+ * kernels use 128-bit loads, but is not required).  C must not overlap A or
+ * B.  The library allocates no device memory and keeps no state between
+ * calls; it is safe to call from several host threads.
+ *
+ * Asynchrony: every call only enqueues work on `stream` (a hipStream_t; 0 is
+ * the null stream) and returns.  Errors detected while the kernels run are
+ * reported by the caller's next synchronising HIP call, not by the return
+ * value.
+ *
+ * Degenerate shapes (the page's harness: negative sizes are an error, an
+ * empty output returns at once, K = 0 leaves the sum empty):
+ *   M < 0, N < 0 or K < 0  -> GEMM_F32_ERR_DIM, nothing is enqueued;
+ *   M == 0 or N == 0       -> GEMM_F32_OK, nothing is enqueued, any pointer
+ *                             may be NULL;
+ *   K == 0                 -> the M x N window of C is set to +0.0; A and B
+ *                             may be NULL.
+ * Only the M x N window of C is written; C[i*ldc + j] for j >= N is left
+ * untouched.
+ */
+#ifndef GEMM_F32_H
+#define GEMM_F32_H
+
+#include <hip/hip_runtime_api.h>
+
+/* Exported from libgemm_f32.so (the library is built with hidden visibility). */
+#define GEMM_F32_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define GEMM_F32_OK          0  /* work enqueued (or nothing to do)            */
+#define GEMM_F32_ERR_DIM     1  /* M, N or K negative, or too large to tile     */
+#define GEMM_F32_ERR_LD      2  /* lda < max(1,K), ldb < max(1,N) or
+                                   ldc < max(1,N)                              */
+#define GEMM_F32_ERR_NULL    3  /* a pointer the shape needs is NULL            */
+#define GEMM_F32_ERR_LAUNCH  4  /* the HIP runtime refused the kernel launch    */
+#define GEMM_F32_ERR_CONFIG  5  /* unknown configuration index                 */
+#define GEMM_F32_ERR_ALIGN   6  /* a pointer is not 4-byte aligned              */
+
+/*
+ * C := A . B on `stream`, with the kernel configuration chosen for the shape
+ * and operand alignment (gemm_f32_describe() names the choice).  Arguments
+ * are validated in this order: sizes, leading dimensions, NULL pointers,
+ * alignment; the first failure is returned and nothing is enqueued.
+ */
+GEMM_F32_API int gemm_f32(int M, int N, int K,
+             const float *A, int lda,
+             const float *B, int ldb,
+             float *C, int ldc,
+             hipStream_t stream);
+
+/*
+ * As gemm_f32(), but with the kernel configuration forced to `config`
+ * (0 <= config < gemm_f32_num_configs(); -1 selects automatically).  Every
+ * configuration handles every shape and alignment, so this exists to test and
+ * to time each kernel on any problem; unknown indices return
+ * GEMM_F32_ERR_CONFIG.
+ */
+GEMM_F32_API int gemm_f32_with_config(int config, int M, int N, int K,
+                         const float *A, int lda,
+                         const float *B, int ldb,
+                         float *C, int ldc,
+                         hipStream_t stream);
+
+/* Number of kernel configurations, and the name of one ("" if unknown). */
+GEMM_F32_API int gemm_f32_num_configs(void);
+GEMM_F32_API const char *gemm_f32_config_name(int config);
+
+/*
+ * Writes into buf (NUL-terminated, at most buflen bytes) a one-line
+ * description of what gemm_f32() would enqueue for these arguments: the
+ * configuration name first ("none" for an empty output, "fill_zero" for
+ * K == 0), then tile grid, workgroup count and load widths.  Pointers are only
+ * inspected for alignment, never dereferenced.  Returns the status gemm_f32()
+ * would return for the same arguments.
+ */
+GEMM_F32_API int gemm_f32_describe(int M, int N, int K,
+                      const float *A, int lda,
+                      const float *B, int ldb,
+                      const float *C, int ldc,
+                      char *buf, int buflen);
+
+/* Static text for a return code. */
+GEMM_F32_API const char *gemm_f32_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_F32_H */

@@ -1,0 +1,111 @@
+"""The C ABI of libgemm_f32.so: exports, argument validation, plan description.
+
+The CPU tests here never launch a kernel: every call either fails validation
+or has an empty output, which the library handles on the host before any HIP
+call.  Launching tests are marked ``gpu``.
+"""
+import re
+import os
+
+import numpy as np
+import pytest
+
+from dense_fp32_gemm_amd import binding as gb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f32.h")
+
+FAKE = 0x100000   # a 4-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"GEMM_F32_API\s+[\w\s\*]*?\b(gemm_f32\w*)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert "gemm_f32" in names and len(names) >= 6
+    lib = gb.load()
+    for n in names:
+        assert hasattr(lib, n), n
+        assert hasattr(gb, n), f"binding lacks {n}"
+
+
+def test_status_codes_match_header():
+    text = open(HEADER).read()
+    for name, value in re.findall(r"#define (GEMM_F32_(?:OK|ERR_\w+))\s+(\d+)", text):
+        assert getattr(gb, name) == int(value), name
+        assert gb.gemm_f32_status_string(int(value)) not in ("", "unknown status")
+
+
+def test_config_names():
+    names = gb.config_names()
+    assert len(names) == gb.gemm_f32_num_configs() >= 2
+    assert names[0].startswith("valu") and any(n.startswith("mfma") for n in names)
+    assert gb.gemm_f32_config_name(-1) == "" and gb.gemm_f32_config_name(len(names)) == ""
+
+
+@pytest.mark.parametrize("M,N,K", [(-1, 4, 4), (4, -1, 4), (4, 4, -1)])
+def test_negative_sizes(M, N, K):
+    assert gb.gemm_f32(M, N, K, FAKE, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_DIM
+
+
+@pytest.mark.parametrize("lda,ldb,ldc", [(7, 9, 9), (8, 8, 9), (8, 9, 8), (0, 9, 9)])
+def test_small_leading_dimension(lda, ldb, ldc):
+    assert gb.gemm_f32(5, 9, 8, FAKE, lda, FAKE, ldb, FAKE, ldc, 0) == gb.GEMM_F32_ERR_LD
+
+
+def test_leading_dimension_minimum_is_one():
+    # K == 0 still needs lda >= 1; N == 0 still needs ldb, ldc >= 1.
+    assert gb.gemm_f32(3, 0, 0, 0, 0, 0, 1, 0, 1, 0) == gb.GEMM_F32_ERR_LD
+    assert gb.gemm_f32(3, 0, 2, 0, 2, 0, 0, 0, 1, 0) == gb.GEMM_F32_ERR_LD
+
+
+def test_null_pointers():
+    assert gb.gemm_f32(4, 4, 4, 0, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_NULL
+    assert gb.gemm_f32(4, 4, 4, FAKE, 4, 0, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_NULL
+    assert gb.gemm_f32(4, 4, 4, FAKE, 4, FAKE, 4, 0, 4, 0) == gb.GEMM_F32_ERR_NULL
+    assert gb.gemm_f32(4, 4, 0, 0, 1, 0, 4, 0, 4, 0) == gb.GEMM_F32_ERR_NULL   # K=0 still writes C
+
+
+def test_misaligned_pointers():
+    assert gb.gemm_f32(4, 4, 4, FAKE + 2, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_ALIGN
+    assert gb.gemm_f32(4, 4, 4, FAKE, 4, FAKE + 1, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_ALIGN
+    assert gb.gemm_f32(4, 4, 4, FAKE, 4, FAKE, 4, FAKE + 3, 4, 0) == gb.GEMM_F32_ERR_ALIGN
+
+
+def test_validation_order():
+    # sizes before leading dimensions before pointers before alignment
+    assert gb.gemm_f32(-1, 4, 4, 0, 0, 0, 0, 0, 0, 0) == gb.GEMM_F32_ERR_DIM
+    assert gb.gemm_f32(4, 4, 4, 0, 0, 0, 4, 0, 4, 0) == gb.GEMM_F32_ERR_LD
+    assert gb.gemm_f32(4, 4, 4, 0, 4, FAKE + 1, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_NULL
+
+
+def test_unknown_config():
+    n = gb.gemm_f32_num_configs()
+    for c in (-2, n, n + 7):
+        assert gb.gemm_f32_with_config(c, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_CONFIG
+
+
+@pytest.mark.parametrize("M,N", [(0, 5), (5, 0), (0, 0)])
+def test_empty_output_is_ok_without_pointers(M, N):
+    assert gb.gemm_f32(M, N, 7, 0, 7, 0, max(N, 1), 0, max(N, 1), 0) == gb.GEMM_F32_OK
+
+
+def test_describe():
+    rc, text = gb.gemm_f32_describe(0, 5, 3, 0, 3, 0, 5, 0, 5)
+    assert rc == gb.GEMM_F32_OK and text == "none"
+    rc, text = gb.gemm_f32_describe(5, 5, 0, 0, 1, 0, 5, FAKE, 5)
+    assert rc == gb.GEMM_F32_OK and text == "fill_zero"
+    rc, text = gb.gemm_f32_describe(-1, 5, 3, 0, 3, 0, 5, 0, 5)
+    assert rc == gb.GEMM_F32_ERR_DIM and text.startswith("invalid")
+    rc, text = gb.gemm_f32_describe(8192, 8192, 8192, FAKE, 8192, FAKE, 8192, FAKE, 8192)
+    assert rc == gb.GEMM_F32_OK and text.startswith("mfma") and "load_a=x4 load_b=x4" in text
+    rc, text = gb.gemm_f32_describe(1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
+    assert rc == gb.GEMM_F32_OK and "load_a=x4 load_b=x1" in text
+    rc, text = gb.gemm_f32_describe(1, 1, 1, FAKE, 1, FAKE, 1, FAKE, 1)
+    assert rc == gb.GEMM_F32_OK and text.startswith("valu")
+    # 16-byte alignment of the base decides the load width as well
+    rc, text = gb.gemm_f32_describe(512, 512, 512, FAKE + 4, 512, FAKE, 512, FAKE, 512)
+    assert "load_a=x1 load_b=x4" in text

@@ -1,0 +1,240 @@
+"""GPU parity: libgemm_f32.so (through its C ABI) against the CPU oracle.
+
+Acceptance (tests/checks.py): bit-exact on quarter-step operands, where every
+binary32 partial sum is exact and the product is unique; otherwise
+|gpu - oracle| <= 1e-3 + 1e-3 * |oracle| per element.
+
+Workloads: 512^3 quarter-step; the boundary set (1025,1023,1000), (1,1,1),
+(17,33,65), (1000,1000,1000) on uniform[-1,1); 2048^3 uniform and
+quarter-step (full oracle); 8192^3 and the rectangular sweep (8192,8192,128),
+(16384,64,4096), (64,16384,4096), (4096,4096,16384) on uniform operands,
+checked on 4096 seeded sample positions in the configuration the benchmark
+times.  Small ragged shapes run on every kernel configuration.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_fp32_gemm_amd import binding as gb
+from dense_fp32_gemm_amd import inputs
+from checks import assert_bit_exact, assert_close
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+CONFIGS = list(range(gb.gemm_f32_num_configs()))
+CONFIG_IDS = [gb.gemm_f32_config_name(c) for c in CONFIGS]
+
+
+def say(*msg):
+    """Names the case before each GPU step (visible with pytest -s)."""
+    print("[parity]", *msg, file=sys.__stderr__, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say("device:", torch.cuda.get_device_name(0))
+    return torch.device("cuda:0")
+
+
+@functools.lru_cache(maxsize=4)
+def operands(kind, M, N, K):
+    if kind == "uniform":
+        return inputs.uniform(M, N, K)
+    return inputs.quarter_step(M, N, K)
+
+
+def gpu_gemm(A, B, config=-1, dev=None, pad=(0, 0, 0), offset=(0, 0, 0), sentinel=np.nan):
+    """Runs gemm_f32 on copies of A and B; returns (C window, full C buffer).
+
+    pad adds columns to each operand's leading dimension; offset shifts each
+    operand's base address by that many floats (4-byte aligned only).  The
+    C buffer starts filled with `sentinel`.
+    """
+    M, K = A.shape
+    N = B.shape[1]
+    lda, ldb, ldc = max(1, K) + pad[0], max(1, N) + pad[1], max(1, N) + pad[2]
+    dA = torch.full((offset[0] + M * lda + 1,), np.nan, dtype=torch.float32, device=dev)
+    dB = torch.full((offset[1] + K * ldb + 1,), np.nan, dtype=torch.float32, device=dev)
+    dC = torch.full((offset[2] + M * ldc + 1,), sentinel, dtype=torch.float32, device=dev)
+    if M and K:
+        dA[offset[0]:offset[0] + M * lda].view(M, lda)[:, :K].copy_(torch.from_numpy(A))
+    if K and N:
+        dB[offset[1]:offset[1] + K * ldb].view(K, ldb)[:, :N].copy_(torch.from_numpy(B))
+    say(f"gemm_f32 config={config} M={M} N={N} K={K} ld=({lda},{ldb},{ldc}) off={offset}")
+    rc = gb.gemm_f32_with_config(
+        config, M, N, K,
+        dA.data_ptr() + 4 * offset[0], lda,
+        dB.data_ptr() + 4 * offset[1], ldb,
+        dC.data_ptr() + 4 * offset[2], ldc,
+        torch.cuda.current_stream().cuda_stream)
+    assert rc == gb.GEMM_F32_OK, gb.gemm_f32_status_string(rc)
+    torch.cuda.synchronize()
+    full = dC.cpu().numpy()
+    win = full[offset[2]:offset[2] + M * ldc].reshape(M, ldc)[:, :N] if M else np.zeros((0, N), np.float32)
+    return np.ascontiguousarray(win), full
+
+
+# ---------------------------------------------------------------------------
+# The workloads
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("config", [-1] + CONFIGS, ids=["auto"] + CONFIG_IDS)
+def test_512_quarter_step_bit_exact(dev, config):
+    A, B = operands("quarter", 512, 512, 512)
+    got, _ = gpu_gemm(A, B, config, dev)
+    assert_bit_exact(got, oracle.gemm(A, B), f"512^3 quarter-step config {config}")
+
+
+BOUNDARY = [(1025, 1023, 1000), (1, 1, 1), (17, 33, 65), (1000, 1000, 1000)]
+
+
+@pytest.mark.parametrize("config", [-1] + CONFIGS, ids=["auto"] + CONFIG_IDS)
+@pytest.mark.parametrize("shape", BOUNDARY, ids=lambda s: "x".join(map(str, s)))
+def test_boundary_set_uniform(dev, shape, config):
+    A, B = operands("uniform", *shape)
+    got, _ = gpu_gemm(A, B, config, dev)
+    assert_close(got, oracle.gemm(A, B), f"{shape} config {config}")
+
+
+def test_2048_uniform_full(dev):
+    A, B = operands("uniform", 2048, 2048, 2048)
+    got, _ = gpu_gemm(A, B, -1, dev)
+    assert_close(got, oracle.gemm(A, B), "2048^3 uniform")
+
+
+def test_2048_quarter_step_bit_exact(dev):
+    A, B = operands("quarter", 2048, 2048, 2048)
+    got, _ = gpu_gemm(A, B, -1, dev)
+    assert_bit_exact(got, oracle.gemm(A, B), "2048^3 quarter-step")
+
+
+LARGE = [(8192, 8192, 8192), (8192, 8192, 128), (16384, 64, 4096),
+         (64, 16384, 4096), (4096, 4096, 16384)]
+
+
+@pytest.mark.parametrize("shape", LARGE, ids=lambda s: "x".join(map(str, s)))
+def test_large_sampled(dev, shape):
+    M, N, K = shape
+    A, B = inputs.uniform(M, N, K)
+    got, _ = gpu_gemm(A, B, -1, dev, sentinel=np.nan)
+    r, c = inputs.sample_positions(M, N)
+    assert_close(got[r, c], oracle.gemm_at(A, B, r, c), f"{shape} sampled")
+    # every element was written and is finite (the buffer started as NaN)
+    assert np.isfinite(got).all()
+
+
+# ---------------------------------------------------------------------------
+# Every configuration on ragged shapes: several tiles plus a partial one in
+# each dimension, K not a multiple of the panel depth.
+# ---------------------------------------------------------------------------
+RAGGED = [(300, 270, 77), (513, 385, 129), (97, 1100, 45), (1100, 70, 300), (33, 31, 2)]
+
+
+@pytest.mark.parametrize("config", CONFIGS, ids=CONFIG_IDS)
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+def test_ragged_bit_exact(dev, shape, config):
+    A, B = operands("quarter", *shape)
+    got, _ = gpu_gemm(A, B, config, dev)
+    assert_bit_exact(got, oracle.gemm(A, B), f"{shape} config {config}")
+
+
+@pytest.mark.parametrize("config", CONFIGS, ids=CONFIG_IDS)
+def test_permutation_pins_lane_layout(dev, config):
+    """X @ P and P @ Y are exact permutations: any lane/register mix-up in
+    operand or accumulator mapping moves a value to the wrong place."""
+    n, m = 300, 260
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(n)
+    P = np.zeros((n, n), np.float32)
+    P[np.arange(n), perm] = 1.0
+    X, _ = inputs.uniform(m, 1, n)
+    want = np.empty_like(X)
+    want[:, perm] = X
+    got, _ = gpu_gemm(X, P, config, dev)
+    assert_bit_exact(got, want, "X @ P")
+    Y = np.ascontiguousarray(X.T)
+    got, _ = gpu_gemm(P, Y, config, dev)
+    assert_bit_exact(got, Y[perm], "P @ Y")
+
+
+@pytest.mark.parametrize("config", CONFIGS, ids=CONFIG_IDS)
+def test_leading_dimensions_keep_padding(dev, config):
+    M, N, K = 130, 200, 72
+    A, B = operands("quarter", M, N, K)
+    got, full = gpu_gemm(A, B, config, dev, pad=(3, 5, 7))
+    assert_bit_exact(got, oracle.gemm(A, B), "padded ld")
+    ldc = N + 7
+    body = full[:M * ldc].reshape(M, ldc)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[M * ldc:]).all()
+
+
+@pytest.mark.parametrize("config", CONFIGS, ids=CONFIG_IDS)
+def test_unaligned_bases(dev, config):
+    """Bases 4-byte but not 16-byte aligned take the 32-bit load path."""
+    M, N, K = 200, 160, 96
+    A, B = operands("quarter", M, N, K)
+    got, full = gpu_gemm(A, B, config, dev, offset=(1, 3, 2))
+    assert_bit_exact(got, oracle.gemm(A, B), "offset bases")
+    assert np.isnan(full[:2]).all()
+
+
+def test_k_zero_writes_positive_zero(dev):
+    A = np.zeros((37, 0), np.float32)
+    B = np.zeros((0, 45), np.float32)
+    got, full = gpu_gemm(A, B, -1, dev, pad=(1, 0, 3))
+    assert_bit_exact(got, np.zeros((37, 45), np.float32), "K=0")
+    body = full[:37 * 48].reshape(37, 48)
+    assert np.isnan(body[:, 45:]).all()
+
+
+@pytest.mark.parametrize("M,N", [(0, 17), (17, 0)])
+def test_empty_output_touches_nothing(dev, M, N):
+    A, B = operands("uniform", M, N, 5)
+    got, full = gpu_gemm(A, B, -1, dev)
+    assert got.shape == (M, N) and np.isnan(full).all()
+
+
+def test_transpose_invariant(dev):
+    """(A B)^T = B^T A^T, bit-exact on quarter-step operands."""
+    M, N, K = 384, 260, 200
+    A, B = operands("quarter", M, N, K)
+    C, _ = gpu_gemm(A, B, -1, dev)
+    Ct, _ = gpu_gemm(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T), -1, dev)
+    assert_bit_exact(Ct.T, C, "transpose")
+
+
+def test_all_ones_long_k(dev):
+    K = 16384
+    got, _ = gpu_gemm(np.ones((256, K), np.float32), np.ones((K, 256), np.float32), -1, dev)
+    assert_bit_exact(got, np.full((256, 256), K, np.float32), "all-ones")
+
+
+def test_identity_is_exact(dev):
+    A, _ = operands("uniform", 1000, 1, 1000)
+    got, _ = gpu_gemm(A, np.eye(1000, dtype=np.float32), -1, dev)
+    assert_bit_exact(got, A, "A @ I")
+
+
+def test_rank1_k1_is_one_rounding(dev):
+    A, B = operands("uniform", 700, 900, 1)
+    got, _ = gpu_gemm(A, B, -1, dev)
+    assert_bit_exact(got, A * B, "K=1")
+
+
+def test_runs_on_a_side_stream_and_repeats_bit_identically(dev):
+    A, B = operands("uniform", 1000, 1000, 1000)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c1 = gb.matmul(dA, dB)
+        c2 = gb.matmul(dA, dB)
+    s.synchronize()
+    assert torch.equal(c1, c2)
+    assert_close(c1.cpu().numpy(), oracle.gemm(A, B), "side stream")
