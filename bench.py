@@ -15,6 +15,8 @@ shape (on stderr).  The last stdout line is one JSON object.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -70,7 +72,8 @@ def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1):
     wall = time.perf_counter() - t0
     ev = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])   # ms
     flop = 2.0 * M * N * K
-    rc, desc = gb.gemm_f32_describe(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+    rc, desc = gb.gemm_f32_describe(config, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                                    dC.data_ptr(), N)
     out = {
         "M": M, "N": N, "K": K, "kernel": desc,
         "wall_ms_per_step": 1e3 * wall / steps,
@@ -84,6 +87,21 @@ def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1):
     del dA, dB, dC
     torch.cuda.empty_cache()
     return out
+
+
+def measured_traffic(kernel_desc, M, N, K):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    record for this kernel and shape, or None if there is none or the kernel
+    source has changed since the counters were taken."""
+    src = os.path.join(ROOT, "dense_fp32_gemm_amd", "csrc", "gemm_f32.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    name = kernel_desc.split()[0]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
+        rec = json.load(open(path))
+        if (rec.get("kernel") == name and rec.get("workload") == f"{M}x{N}x{K}"
+                and rec.get("source_sha256") == sha):
+            return int(round(rec["bytes_per_launch"]))
+    return None
 
 
 def cpu_baseline(M, N, K, budget_s=12.0):
@@ -116,6 +134,9 @@ def main():
     ap.add_argument("--config", type=int, default=-1)
     ap.add_argument("--table", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-mib", type=int, default=0,
+                    help="also run an elementwise copy (torch.neg) of this many MiB, "
+                         "the known-size kernel that scales HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -130,6 +151,16 @@ def main():
         sys.exit(1)
     gb.load()
     log(f"device: {torch.cuda.get_device_name(0)}")
+
+    if args.calibrate_mib:
+        n = args.calibrate_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"calibration: torch.neg over {args.calibrate_mib} MiB read + {args.calibrate_mib} MiB written, 3 launches")
+        del src, dst
 
     M, N, K = args.shape
     head = time_gemm(torch, gb, M, N, K, args.steps, args.warmup, args.config)
@@ -163,7 +194,8 @@ def main():
                    "pct_of_fp32_matrix_peak": round(100.0 * head["tflops_wall"] / PEAK_FP32_MATRIX_TFLOPS, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
                      "peak": PEAK_FP32_MATRIX_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
+                     "traffic": measured_traffic(head["kernel"], M, N, K)},
     }
     if extra:
         line["config"]["other_tflops"] = extra

@@ -49,7 +49,7 @@ def load() -> ctypes.CDLL:
         lib.gemm_f32_num_configs.restype = i
         lib.gemm_f32_config_name.argtypes = [i]
         lib.gemm_f32_config_name.restype = ctypes.c_char_p
-        lib.gemm_f32_describe.argtypes = [i, i, i, p, i, p, i, p, i, ctypes.c_char_p, i]
+        lib.gemm_f32_describe.argtypes = [i, i, i, i, p, i, p, i, p, i, ctypes.c_char_p, i]
         lib.gemm_f32_describe.restype = i
         lib.gemm_f32_status_string.argtypes = [i]
         lib.gemm_f32_status_string.restype = ctypes.c_char_p
@@ -75,10 +75,10 @@ def gemm_f32_config_name(config: int) -> str:
     return load().gemm_f32_config_name(config).decode()
 
 
-def gemm_f32_describe(M, N, K, A, lda, B, ldb, C, ldc) -> tuple[int, str]:
-    """(status, description) of what gemm_f32 would enqueue."""
+def gemm_f32_describe(config, M, N, K, A, lda, B, ldb, C, ldc) -> tuple[int, str]:
+    """(status, description) of what gemm_f32_with_config would enqueue."""
     buf = ctypes.create_string_buffer(256)
-    rc = load().gemm_f32_describe(M, N, K, A, lda, B, ldb, C, ldc, buf, len(buf))
+    rc = load().gemm_f32_describe(config, M, N, K, A, lda, B, ldb, C, ldc, buf, len(buf))
     return rc, buf.value.decode()
 
 

@@ -101,7 +101,7 @@ __device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncol
 // ---------------------------------------------------------------------------
 // Matrix-core kernel
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, bool PRIO_ = false, int GROUP_ = 8>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -122,7 +122,8 @@ struct MfmaTile {
     // 4-element chunks each thread moves per panel.
     static constexpr int kChunksA = BM * BK / 4 / kThreads;
     static constexpr int kChunksB = BK * BN / 4 / kThreads;
-    static constexpr int kGroup = 8;                 // tile rows per raster group
+    static constexpr int kGroup = GROUP_;            // tile rows per raster group
+    static constexpr bool kPrio = PRIO_;             // raise wave priority for MFMA bursts
 
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
     static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
@@ -243,6 +244,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 #pragma unroll
                     for (int j = 0; j < T::kFragN; ++j)
                         b[s][j] = lb[(8 * kg + s) * T::kStrideB + j * 32];
+                if (T::kPrio)
+                    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -250,6 +253,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 #pragma unroll
                         for (int j = 0; j < T::kFragN; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
+                if (T::kPrio)
+                    __builtin_amdgcn_s_setprio(0);
             }
             __syncthreads();
         }
@@ -259,6 +264,187 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
         for (int i = 0; i < T::kFragM; ++i) {
 #pragma unroll
             for (int j = 0; j < T::kFragN; ++j) {
+                const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                    if (row < g.M && col < g.N)
+                        g.C[(int64_t)row * g.ldc + col] = acc[i][j][r];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Matrix-core kernel with direct-to-LDS operand loads.
+//
+// gfx950 buffer loads can write their result straight into LDS
+// (buffer_load_dword[x4] ... lds): lane l of a wave deposits its 4 or 16
+// bytes at LDS base + l*size, so one wave instruction fills 256 B or 1 KB of
+// LDS with no VGPR staging and no ds_write.  Which global element lands in
+// which LDS slot is chosen through the per-lane global offset, which is how
+// the bank-conflict-avoiding layouts below are produced.  A buffer offset
+// outside the resource's range reads as zero, so ragged rows, columns and
+// K-tails are zero-filled by pointing their lanes at an out-of-range offset.
+//
+// LDS layouts (per panel, BK = 16):
+//  * A: [BM][16] floats, the four 16-byte chunks of row r permuted by
+//    chunk ^ swz_a(r).  A half-wave's 128-bit fragment reads (32 rows, one
+//    chunk) then touch every bank exactly once.
+//  * B: [16][BN] floats; in rows with bit 2 of k set, columns are stored at
+//    col ^ 32.  The two lane halves read rows k and k+4 (same columns), which
+//    the swap moves onto different banks.
+// Buffer resources are rebased on every panel (A at row m0 / column k0, B at
+// row k0 / column n0), so every in-range offset stays below 2^31.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as 0
+constexpr int kRawBufferFlags = 0x00020000;      // dword 3 of a raw buffer resource
+
+__device__ inline int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+__device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_base, uint32_t offset, int bytes)
+{
+    auto *dst = (__attribute__((address_space(3))) void *)lds_base;
+    if (bytes == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, offset, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, offset, 0, 0, 0);
+}
+
+template <class T, bool VEC_A, bool VEC_B>
+__global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
+{
+    constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
+    constexpr int NW = T::kThreads / kWaveSize;
+    constexpr int FM = T::kFragM, FN = T::kFragN;
+    static_assert(BK == 16, "the A layout permutes four 16-byte chunks per row");
+    static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
+    constexpr int kA = BM * BK;                       // floats per A panel
+    constexpr int kB = BK * BN;                       // floats per B panel
+    constexpr int kVecA = VEC_A ? 4 : 1, kVecB = VEC_B ? 4 : 1;
+    constexpr int kSpanA = kWaveSize * kVecA;         // floats one instruction moves
+    constexpr int kSpanB = kWaveSize * kVecB;
+    constexpr int kLoadsA = kA / kSpanA / NW;         // instructions per wave per panel
+    constexpr int kLoadsB = kB / kSpanB / NW;
+    static_assert(kA % (kSpanA * NW) == 0 && kB % (kSpanB * NW) == 0, "panel split");
+    __shared__ __attribute__((aligned(1024))) float lds[2][kA + kB];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWaveSize;
+    const int wave = tid / kWaveSize;
+    const int wave_m = wave / T::WAVES_N;
+    const int wave_n = wave % T::WAVES_N;
+    const int li = lane % 32;
+    const int lh = lane / 32;
+
+    // Slot -> source element maps, fixed for the whole kernel.
+    uint32_t a_off[kLoadsA];     // byte offset from the panel's (m0, k0) corner
+    int a_r[kLoadsA], a_k[kLoadsA];
+#pragma unroll
+    for (int j = 0; j < kLoadsA; ++j) {
+        const int f = (wave * kLoadsA + j) * kSpanA + lane * kVecA;   // LDS slot (float index)
+        const int r = f / BK, e = f % BK;
+        const int k = 4 * ((e / 4) ^ swz_a(r)) + e % 4;
+        a_r[j] = r;
+        a_k[j] = k;
+        a_off[j] = (uint32_t)(r * g.lda + k) * 4u;
+    }
+    uint32_t b_off[kLoadsB];
+    int b_k[kLoadsB], b_c[kLoadsB];
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j) {
+        const int f = (wave * kLoadsB + j) * kSpanB + lane * kVecB;
+        const int k = f / BN;
+        const int c = (f % BN) ^ (((k >> 2) & 1) * 32);
+        b_k[j] = k;
+        b_c[j] = c;
+        b_off[j] = (uint32_t)(k * g.ldb + c) * 4u;
+    }
+    // Fragment read addresses (floats within a panel buffer).
+    const int a_frag = (wave_m * T::kWaveM + li) * BK;
+    const int a_swz = swz_a(li);
+    // Column of fragment j after the half swap of rows with bit 2 of k set
+    // (k = 8q + 4*lh + s, so that bit is lh); the fragment base is a multiple
+    // of 32, so the swap only flips its bit 5.
+    int b_frag[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+        b_frag[j] = kA + (4 * lh) * BN + (((wave_n * T::kWaveN + 32 * j) ^ (32 * lh)) + li);
+
+    const int total = g.tiles_m * g.tiles_n;
+    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+        const int t = (int)gridDim.x == total ? xcd_contiguous(w, total) : w;
+        int tm, tn;
+        tile_coords(t, g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
+        const int m0 = tm * BM;
+        const int n0 = tn * BN;
+
+        auto issue = [&](int buf, int k0) {
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(g.A + ((int64_t)m0 * g.lda + k0)), 0, (int)kOutOfRange, kRawBufferFlags);
+#pragma unroll
+            for (int j = 0; j < kLoadsA; ++j) {
+                const bool ok = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K;
+                buffer_to_lds(ra, &lds[buf][(wave * kLoadsA + j) * kSpanA], ok ? a_off[j] : kOutOfRange, 4 * kVecA);
+            }
+            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0, (int)kOutOfRange, kRawBufferFlags);
+#pragma unroll
+            for (int j = 0; j < kLoadsB; ++j) {
+                const bool ok = k0 + b_k[j] < g.K && n0 + b_c[j] < g.N;
+                buffer_to_lds(rb, &lds[buf][kA + (wave * kLoadsB + j) * kSpanB], ok ? b_off[j] : kOutOfRange, 4 * kVecB);
+            }
+        };
+
+        f32x16 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.f;
+
+        const int ktiles = (g.K + BK - 1) / BK;
+        issue(0, 0);
+        __syncthreads();
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int cur = kt & 1;
+            // Buffer cur^1 was last read before the previous barrier.
+            if (kt + 1 < ktiles)
+                issue(cur ^ 1, (kt + 1) * BK);
+            const float *pa = lds[cur] + a_frag;
+            const float *pb = lds[cur];
+#pragma unroll
+            for (int q = 0; q < BK / 8; ++q) {
+                f32x4 a[FM];
+                float b[4][FN];
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+                    a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz));
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
+            }
+            // Waits for this wave's loads of the next panel and its reads of
+            // this one, then for every other wave.
+            __syncthreads();
+        }
+
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
                 const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -350,74 +536,124 @@ __global__ __launch_bounds__(256) void fill_zero(float *C, int64_t ldc, int M, i
 // ---------------------------------------------------------------------------
 // Configurations
 // ---------------------------------------------------------------------------
-using Tile256x128 = MfmaTile<256, 128, 16, 2, 2>;   // wave 128 x 64, 8 accumulators
-using Tile128x256 = MfmaTile<128, 256, 16, 2, 2>;   // wave 64 x 128
-using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;   // wave 64 x 64, 4 accumulators
-using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;     // wave 64 x 32
-using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;     // wave 32 x 64
-using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;       // wave 32 x 32, 1 accumulator
+using Tile256x256 = MfmaTile<256, 256, 16, 2, 4>;   // 8 waves of 128 x 64
+using Tile256x128 = MfmaTile<256, 128, 16, 2, 2>;   // 4 waves of 128 x 64
+using Tile128x256 = MfmaTile<128, 256, 16, 2, 2>;   // 4 waves of 64 x 128
+using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;   // 4 waves of 64 x 64
+using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;     // 4 waves of 64 x 32
+using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;     // 4 waves of 32 x 64
+using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;       // 4 waves of 32 x 32
 
 enum ConfigId {
     kCfgValu64 = 0,
-    kCfgMfma256x128,
-    kCfgMfma128x256,
-    kCfgMfma128x128,
-    kCfgMfma128x64,
-    kCfgMfma64x128,
-    kCfgMfma64x64,
+    kCfgDma256x256,
+    kCfgDma256x128,
+    kCfgDma128x256,
+    kCfgDma128x128,
+    kCfgDma128x64,
+    kCfgDma64x128,
+    kCfgDma64x64,
+    kCfgStaged256x256,
+    kCfgStaged128x128,
+    kCfgStaged64x64,
     kNumConfigs
 };
 
 struct ConfigInfo {
     const char *name;
     int bm, bn, threads;
+    bool dma;
 };
 
 const ConfigInfo kConfigs[kNumConfigs] = {
-    {"valu_64x64", kValuTile, kValuTile, kValuThreads},
-    {"mfma_256x128x16", 256, 128, Tile256x128::kThreads},
-    {"mfma_128x256x16", 128, 256, Tile128x256::kThreads},
-    {"mfma_128x128x16", 128, 128, Tile128x128::kThreads},
-    {"mfma_128x64x16", 128, 64, Tile128x64::kThreads},
-    {"mfma_64x128x16", 64, 128, Tile64x128::kThreads},
-    {"mfma_64x64x16", 64, 64, Tile64x64::kThreads},
+    {"valu_64x64", kValuTile, kValuTile, kValuThreads, false},
+    {"dma_256x256x16", 256, 256, Tile256x256::kThreads, true},
+    {"dma_256x128x16", 256, 128, Tile256x128::kThreads, true},
+    {"dma_128x256x16", 128, 256, Tile128x256::kThreads, true},
+    {"dma_128x128x16", 128, 128, Tile128x128::kThreads, true},
+    {"dma_128x64x16", 128, 64, Tile128x64::kThreads, true},
+    {"dma_64x128x16", 64, 128, Tile64x128::kThreads, true},
+    {"dma_64x64x16", 64, 64, Tile64x64::kThreads, true},
+    {"staged_256x256x16", 256, 256, Tile256x256::kThreads, false},
+    {"staged_128x128x16", 128, 128, Tile128x128::kThreads, false},
+    {"staged_64x64x16", 64, 64, Tile64x64::kThreads, false},
 };
+
+template <class T, template <class, bool, bool> class Kernel>
+struct Launch {
+    static hipError_t run(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
+    {
+        if (va && vb)
+            hipLaunchKernelGGL((Kernel<T, true, true>::fn), dim3(grid), dim3(T::kThreads), 0, s, g);
+        else if (va)
+            hipLaunchKernelGGL((Kernel<T, true, false>::fn), dim3(grid), dim3(T::kThreads), 0, s, g);
+        else if (vb)
+            hipLaunchKernelGGL((Kernel<T, false, true>::fn), dim3(grid), dim3(T::kThreads), 0, s, g);
+        else
+            hipLaunchKernelGGL((Kernel<T, false, false>::fn), dim3(grid), dim3(T::kThreads), 0, s, g);
+        return hipGetLastError();
+    }
+};
+
+// Adapters so one launcher serves both matrix-core kernels.
+template <class T, bool VA, bool VB>
+struct PlainKernel {
+    static constexpr auto fn = gemm_f32_mfma<T, VA, VB>;
+};
+template <class T, bool VA, bool VB>
+struct DmaKernel {
+    static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB>;
+};
+
+template <class T>
+hipError_t launch_dma(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
+{
+    return Launch<T, DmaKernel>::run(g, va, vb, grid, s);
+}
 
 template <class T>
 hipError_t launch_mfma(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
 {
-    if (va && vb)
-        gemm_f32_mfma<T, true, true><<<grid, T::kThreads, 0, s>>>(g);
-    else if (va)
-        gemm_f32_mfma<T, true, false><<<grid, T::kThreads, 0, s>>>(g);
-    else if (vb)
-        gemm_f32_mfma<T, false, true><<<grid, T::kThreads, 0, s>>>(g);
-    else
-        gemm_f32_mfma<T, false, false><<<grid, T::kThreads, 0, s>>>(g);
-    return hipGetLastError();
+    return Launch<T, PlainKernel>::run(g, va, vb, grid, s);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Tile choice by shape.  The largest tile that still gives every compute unit
-// at least one tile (256 CUs) is preferred: bigger tiles re-read less of A
-// and B per FLOP, but too few tiles leave matrix cores idle.
-int select_config(int M, int N, int K)
+constexpr int64_t kComputeUnits = 256;   // MI355X
+
+// The direct-to-LDS kernels address each panel with 32-bit buffer offsets
+// from its corner: the farthest in-range element of an A panel is
+// (BM-1)*lda + BK-1 floats away, of a B panel (BK-1)*ldb + BN-1.
+bool dma_offsets_fit(int bm, int bn, int64_t lda, int64_t ldb)
+{
+    const int64_t limit = (int64_t)kOutOfRange / 4;
+    return (bm - 1) * lda + 16 < limit && 15 * ldb + bn < limit;
+}
+
+// Tile choice by shape, from the configuration sweep (sweep.py) on MI355X.
+// Output tiles are the unit of parallelism and a compute unit needs several
+// waves per SIMD to keep its matrix cores fed, so the rule is: 128 x 128
+// tiles when there are at least four per compute unit (256 CUs), else 64-row
+// or 64-column tiles if there are at least two per CU, else 64 x 64.
+// Problems with fewer than 16 rows or columns use the vector-FMA kernel,
+// where a 32-wide matrix-core block would be mostly padding.
+int select_config(int M, int N, int K, bool dma_ok)
 {
     (void)K;
     if (M < 16 || N < 16)
         return kCfgValu64;
-    const int64_t cus = 256;
     auto tiles = [&](int c) { return ceil_div(M, kConfigs[c].bm) * ceil_div(N, kConfigs[c].bn); };
-    if (tiles(kCfgMfma256x128) >= 2 * cus || tiles(kCfgMfma128x256) >= 2 * cus)
-        return M >= N ? kCfgMfma256x128 : kCfgMfma128x256;
-    if (tiles(kCfgMfma128x128) >= cus)
-        return kCfgMfma128x128;
-    if (M >= N && tiles(kCfgMfma128x64) >= cus)
-        return kCfgMfma128x64;
-    if (N > M && tiles(kCfgMfma64x128) >= cus)
-        return kCfgMfma64x128;
-    return kCfgMfma64x64;
+    if (!dma_ok) {
+        if (tiles(kCfgStaged128x128) >= 4 * kComputeUnits)
+            return kCfgStaged128x128;
+        return kCfgStaged64x64;
+    }
+    if (tiles(kCfgDma128x128) >= 4 * kComputeUnits)
+        return kCfgDma128x128;
+    const int wide = N >= M ? kCfgDma64x128 : kCfgDma128x64;
+    if (tiles(wide) >= 2 * kComputeUnits)
+        return wide;
+    return kCfgDma64x64;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -429,8 +665,9 @@ struct Plan {
     int grid;
 };
 
-// Validates the arguments (sizes, leading dimensions, NULL pointers,
-// alignment, in that order) and fills `plan`; returns a GEMM_F32_* code.
+// Validates the arguments (sizes, leading dimensions, configuration index,
+// NULL pointers, alignment, in that order) and fills `plan`; returns a
+// GEMM_F32_* code.
 int make_plan(int config, int M, int N, int K, const float *A, int lda,
               const float *B, int ldb, const float *C, int ldc, Plan *plan)
 {
@@ -453,7 +690,13 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
         plan->grid = (int)(ceil_div((int64_t)M * N, 256) < 4096 ? ceil_div((int64_t)M * N, 256) : 4096);
         return GEMM_F32_OK;
     }
-    const int c = config >= 0 ? config : select_config(M, N, K);
+    int c = config;
+    if (c < 0) {
+        const bool dma_ok = dma_offsets_fit(128, 128, lda, ldb);
+        c = select_config(M, N, K, dma_ok);
+    } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c].bm, kConfigs[c].bn, lda, ldb)) {
+        return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
+    }
     const int64_t tm = ceil_div(M, kConfigs[c].bm);
     const int64_t tn = ceil_div(N, kConfigs[c].bn);
     if (tm * tn > INT32_MAX)
@@ -490,18 +733,23 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     g.K = K;
     g.tiles_m = p.tiles_m;
     g.tiles_n = p.tiles_n;
+    const bool va = p.vec_a, vb = p.vec_b;
     hipError_t err = hipSuccess;
     switch (p.config) {
     case kCfgValu64:
         gemm_f32_valu<<<p.grid, kValuThreads, 0, stream>>>(g);
         err = hipGetLastError();
         break;
-    case kCfgMfma256x128: err = launch_mfma<Tile256x128>(g, p.vec_a, p.vec_b, p.grid, stream); break;
-    case kCfgMfma128x256: err = launch_mfma<Tile128x256>(g, p.vec_a, p.vec_b, p.grid, stream); break;
-    case kCfgMfma128x128: err = launch_mfma<Tile128x128>(g, p.vec_a, p.vec_b, p.grid, stream); break;
-    case kCfgMfma128x64: err = launch_mfma<Tile128x64>(g, p.vec_a, p.vec_b, p.grid, stream); break;
-    case kCfgMfma64x128: err = launch_mfma<Tile64x128>(g, p.vec_a, p.vec_b, p.grid, stream); break;
-    case kCfgMfma64x64: err = launch_mfma<Tile64x64>(g, p.vec_a, p.vec_b, p.grid, stream); break;
+    case kCfgDma256x256: err = launch_dma<Tile256x256>(g, va, vb, p.grid, stream); break;
+    case kCfgDma256x128: err = launch_dma<Tile256x128>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x256: err = launch_dma<Tile128x256>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x128: err = launch_dma<Tile128x128>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x64: err = launch_dma<Tile128x64>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x128: err = launch_dma<Tile64x128>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x64: err = launch_dma<Tile64x64>(g, va, vb, p.grid, stream); break;
+    case kCfgStaged256x256: err = launch_mfma<Tile256x256>(g, va, vb, p.grid, stream); break;
+    case kCfgStaged128x128: err = launch_mfma<Tile128x128>(g, va, vb, p.grid, stream); break;
+    case kCfgStaged64x64: err = launch_mfma<Tile64x64>(g, va, vb, p.grid, stream); break;
     default: return GEMM_F32_ERR_CONFIG;
     }
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
@@ -530,11 +778,11 @@ const char *gemm_f32_config_name(int config)
     return (config >= 0 && config < kNumConfigs) ? kConfigs[config].name : "";
 }
 
-int gemm_f32_describe(int M, int N, int K, const float *A, int lda, const float *B,
-                      int ldb, const float *C, int ldc, char *buf, int buflen)
+int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
+                      const float *B, int ldb, const float *C, int ldc, char *buf, int buflen)
 {
     Plan p;
-    const int rc = make_plan(-1, M, N, K, A, lda, B, ldb, C, ldc, &p);
+    const int rc = make_plan(config, M, N, K, A, lda, B, ldb, C, ldc, &p);
     if (buf == nullptr || buflen <= 0)
         return rc;
     if (rc != GEMM_F32_OK)

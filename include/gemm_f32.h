@@ -97,17 +97,18 @@ GEMM_F32_API const char *gemm_f32_config_name(int config);
 
 /*
  * Writes into buf (NUL-terminated, at most buflen bytes) a one-line
- * description of what gemm_f32() would enqueue for these arguments: the
+ * description of what gemm_f32_with_config(config, ...) would enqueue for
+ * these arguments (config -1: what gemm_f32() would enqueue): the
  * configuration name first ("none" for an empty output, "fill_zero" for
  * K == 0), then tile grid, workgroup count and load widths.  Pointers are only
- * inspected for alignment, never dereferenced.  Returns the status gemm_f32()
+ * inspected for alignment, never dereferenced.  Returns the status the call
  * would return for the same arguments.
  */
-GEMM_F32_API int gemm_f32_describe(int M, int N, int K,
-                      const float *A, int lda,
-                      const float *B, int ldb,
-                      const float *C, int ldc,
-                      char *buf, int buflen);
+GEMM_F32_API int gemm_f32_describe(int config, int M, int N, int K,
+                                   const float *A, int lda,
+                                   const float *B, int ldb,
+                                   const float *C, int ldc,
+                                   char *buf, int buflen);
 
 /* Static text for a return code. */
 GEMM_F32_API const char *gemm_f32_status_string(int status);

@@ -42,7 +42,8 @@ def test_status_codes_match_header():
 def test_config_names():
     names = gb.config_names()
     assert len(names) == gb.gemm_f32_num_configs() >= 2
-    assert names[0].startswith("valu") and any(n.startswith("mfma") for n in names)
+    assert names[0].startswith("valu") and any(n.startswith("dma") for n in names)
+    assert any(n.startswith("staged") for n in names)
     assert gb.gemm_f32_config_name(-1) == "" and gb.gemm_f32_config_name(len(names)) == ""
 
 
@@ -94,18 +95,44 @@ def test_empty_output_is_ok_without_pointers(M, N):
 
 
 def test_describe():
-    rc, text = gb.gemm_f32_describe(0, 5, 3, 0, 3, 0, 5, 0, 5)
+    rc, text = gb.gemm_f32_describe(-1, 0, 5, 3, 0, 3, 0, 5, 0, 5)
     assert rc == gb.GEMM_F32_OK and text == "none"
-    rc, text = gb.gemm_f32_describe(5, 5, 0, 0, 1, 0, 5, FAKE, 5)
+    rc, text = gb.gemm_f32_describe(-1, 5, 5, 0, 0, 1, 0, 5, FAKE, 5)
     assert rc == gb.GEMM_F32_OK and text == "fill_zero"
-    rc, text = gb.gemm_f32_describe(-1, 5, 3, 0, 3, 0, 5, 0, 5)
+    rc, text = gb.gemm_f32_describe(-1, -1, 5, 3, 0, 3, 0, 5, 0, 5)
     assert rc == gb.GEMM_F32_ERR_DIM and text.startswith("invalid")
-    rc, text = gb.gemm_f32_describe(8192, 8192, 8192, FAKE, 8192, FAKE, 8192, FAKE, 8192)
-    assert rc == gb.GEMM_F32_OK and text.startswith("mfma") and "load_a=x4 load_b=x4" in text
-    rc, text = gb.gemm_f32_describe(1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
+    rc, text = gb.gemm_f32_describe(-1, 8192, 8192, 8192, FAKE, 8192, FAKE, 8192, FAKE, 8192)
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma") and "load_a=x4 load_b=x4" in text
+    rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and "load_a=x4 load_b=x1" in text
-    rc, text = gb.gemm_f32_describe(1, 1, 1, FAKE, 1, FAKE, 1, FAKE, 1)
+    rc, text = gb.gemm_f32_describe(-1, 1, 1, 1, FAKE, 1, FAKE, 1, FAKE, 1)
     assert rc == gb.GEMM_F32_OK and text.startswith("valu")
     # 16-byte alignment of the base decides the load width as well
-    rc, text = gb.gemm_f32_describe(512, 512, 512, FAKE + 4, 512, FAKE, 512, FAKE, 512)
+    rc, text = gb.gemm_f32_describe(-1, 512, 512, 512, FAKE + 4, 512, FAKE, 512, FAKE, 512)
     assert "load_a=x1 load_b=x4" in text
+
+
+def test_wide_rows_fall_back_to_staged_kernels():
+    """Direct-to-LDS kernels address a panel with 32-bit offsets; rows so long
+    that a panel spans 2 GiB select the register-staged kernels instead, and
+    forcing a direct-to-LDS configuration is refused."""
+    lda = 1 << 26                      # 128 rows of A span 32 GiB
+    rc, text = gb.gemm_f32_describe(-1, 4096, 4096, 1000, FAKE, lda, FAKE, 4096, FAKE, 4096)
+    assert rc == gb.GEMM_F32_OK and text.startswith("staged"), text
+    dma = [i for i, n in enumerate(gb.config_names()) if n.startswith("dma")]
+    for c in dma:
+        rc, _ = gb.gemm_f32_describe(c, 4096, 4096, 1000, FAKE, lda, FAKE, 4096, FAKE, 4096)
+        assert rc == gb.GEMM_F32_ERR_CONFIG
+    ldb = 1 << 27                      # 16 rows of B span 8 GiB
+    rc, text = gb.gemm_f32_describe(-1, 4096, 4096, 1000, FAKE, 1000, FAKE, ldb, FAKE, 4096)
+    assert text.startswith("staged"), text
+
+
+@pytest.mark.parametrize("shape,name", [
+    ((8192, 8192, 8192), "dma_128x128"), ((2048, 2048, 2048), "dma_64x128"),
+    ((1000, 1000, 1000), "dma_64x64"), ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
+])
+def test_selection(shape, name):
+    M, N, K = shape
+    rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
+    assert rc == gb.GEMM_F32_OK and text.startswith(name), text
