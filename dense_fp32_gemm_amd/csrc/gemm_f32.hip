@@ -101,35 +101,37 @@ __device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncol
 // ---------------------------------------------------------------------------
 // Matrix-core kernel
 // ---------------------------------------------------------------------------
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, bool PRIO_ = false, int GROUP_ = 8>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KSPLIT_ = 1, int STAGES_ = 2,
+          int GROUP_ = 8>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-    static constexpr int kThreads = WAVES_M * WAVES_N * kWaveSize;
+    // K-split inside the workgroup: KSPLIT groups of WAVES_M x WAVES_N waves
+    // each accumulate every KSPLIT-th K-panel of the same output tile.
+    static constexpr int kSplit = KSPLIT_;
+    static constexpr int kGroupWaves = WAVES_M * WAVES_N;
+    static constexpr int kThreads = kGroupWaves * kWaveSize * kSplit;
     static constexpr int kWaveM = BM / WAVES_M;      // C rows per wave
     static constexpr int kWaveN = BN / WAVES_N;      // C columns per wave
     static constexpr int kFragM = kWaveM / 32;       // 32x32 accumulators down
     static constexpr int kFragN = kWaveN / 32;       // 32x32 accumulators across
-    // LDS panels.  A is kept row-major ([m][k], k contiguous) so one 128-bit
-    // read gives a lane 4 consecutive k of its row; the +4 pad makes the 32
-    // rows read by a half-wave fall on distinct banks.  B is kept row-major
-    // ([k][n]); lanes read consecutive n, and the +8 pad puts the two
-    // half-waves (k and k+4) on different banks.
+    // Register-staged kernel's LDS panels.  A is kept row-major ([m][k], k
+    // contiguous) so one 128-bit read gives a lane 4 consecutive k of its row;
+    // the +4 pad makes the 32 rows read by a half-wave fall on distinct banks.
+    // B is kept row-major ([k][n]); lanes read consecutive n, and the +8 pad
+    // puts the two half-waves (k and k+4) on different banks.
     static constexpr int kStrideA = BK + 4;
     static constexpr int kStrideB = BN + 8;
     static constexpr int kLdsA = BM * kStrideA;
     static constexpr int kLdsB = BK * kStrideB;
-    // 4-element chunks each thread moves per panel.
+    // 4-element chunks each thread moves per panel (register-staged kernel).
     static constexpr int kChunksA = BM * BK / 4 / kThreads;
     static constexpr int kChunksB = BK * BN / 4 / kThreads;
     static constexpr int kGroup = GROUP_;            // tile rows per raster group
-    static constexpr bool kPrio = PRIO_;             // raise wave priority for MFMA bursts
+    static constexpr int kStages = STAGES_;          // LDS panel buffers per K-split group
 
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
     static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
-    static_assert(BM * BK % (4 * kThreads) == 0 && kChunksA >= 1, "A panel split");
-    static_assert(BK * BN % (4 * kThreads) == 0 && kChunksB >= 1, "B panel split");
-    static_assert(2 * (kLdsA + kLdsB) * 4 <= 160 * 1024, "LDS budget");
 };
 
 // One v_mfma_f32_32x32x2_f32 adds, for the 32 x 32 block it accumulates,
@@ -146,6 +148,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
     constexpr int NT = T::kThreads;
+    static_assert(T::kSplit == 1 && T::kStages == 2, "the register-staged kernel is double-buffered, unsplit");
+    static_assert(BM * BK % (4 * NT) == 0 && T::kChunksA >= 1, "A panel split");
+    static_assert(BK * BN % (4 * NT) == 0 && T::kChunksB >= 1, "B panel split");
+    static_assert(2 * (T::kLdsA + T::kLdsB) * 4 <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) float lds_a[2][T::kLdsA];
     __shared__ __attribute__((aligned(16))) float lds_b[2][T::kLdsB];
 
@@ -244,8 +250,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 #pragma unroll
                     for (int j = 0; j < T::kFragN; ++j)
                         b[s][j] = lb[(8 * kg + s) * T::kStrideB + j * 32];
-                if (T::kPrio)
-                    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -253,8 +257,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 #pragma unroll
                         for (int j = 0; j < T::kFragN; ++j)
                             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
-                if (T::kPrio)
-                    __builtin_amdgcn_s_setprio(0);
             }
             __syncthreads();
         }
@@ -316,25 +318,35 @@ template <class T, bool VEC_A, bool VEC_B>
 __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
-    constexpr int NW = T::kThreads / kWaveSize;
+    constexpr int NW = T::kGroupWaves;                // waves per K-split group
+    constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
     static_assert(BK == 16, "the A layout permutes four 16-byte chunks per row");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
     constexpr int kA = BM * BK;                       // floats per A panel
     constexpr int kB = BK * BN;                       // floats per B panel
+    constexpr int kStage = kA + kB;
     constexpr int kVecA = VEC_A ? 4 : 1, kVecB = VEC_B ? 4 : 1;
     constexpr int kSpanA = kWaveSize * kVecA;         // floats one instruction moves
     constexpr int kSpanB = kWaveSize * kVecB;
     constexpr int kLoadsA = kA / kSpanA / NW;         // instructions per wave per panel
     constexpr int kLoadsB = kB / kSpanB / NW;
     static_assert(kA % (kSpanA * NW) == 0 && kB % (kSpanB * NW) == 0, "panel split");
-    __shared__ __attribute__((aligned(1024))) float lds[2][kA + kB];
+    constexpr int S = T::kStages;
+    constexpr int kLoads = kLoadsA + kLoadsB;         // per wave per round
+    static_assert(S >= 2 && (S - 2) * kLoads <= 63, "vmcnt range");
+    static_assert(KS * S * kStage * 4 <= 160 * 1024, "LDS budget");
+    static_assert(KS == 1 || KS * S * kStage >= BM * BN, "the K-split reduction reuses the panel buffers");
+    // Each K-split group owns S panel buffers, used as a ring.
+    __shared__ __attribute__((aligned(1024))) float lds[KS][S][kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWaveSize;
     const int wave = tid / kWaveSize;
-    const int wave_m = wave / T::WAVES_N;
-    const int wave_n = wave % T::WAVES_N;
+    const int group = KS == 1 ? 0 : wave / NW;        // K-split group
+    const int gw = KS == 1 ? wave : wave % NW;        // wave within its group
+    const int wave_m = gw / T::WAVES_N;
+    const int wave_n = gw % T::WAVES_N;
     const int li = lane % 32;
     const int lh = lane / 32;
 
@@ -343,7 +355,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     int a_r[kLoadsA], a_k[kLoadsA];
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
-        const int f = (wave * kLoadsA + j) * kSpanA + lane * kVecA;   // LDS slot (float index)
+        const int f = (gw * kLoadsA + j) * kSpanA + lane * kVecA;   // LDS slot (float index)
         const int r = f / BK, e = f % BK;
         const int k = 4 * ((e / 4) ^ swz_a(r)) + e % 4;
         a_r[j] = r;
@@ -354,7 +366,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     int b_k[kLoadsB], b_c[kLoadsB];
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
-        const int f = (wave * kLoadsB + j) * kSpanB + lane * kVecB;
+        const int f = (gw * kLoadsB + j) * kSpanB + lane * kVecB;
         const int k = f / BN;
         const int c = (f % BN) ^ (((k >> 2) & 1) * 32);
         b_k[j] = k;
@@ -372,6 +384,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     for (int j = 0; j < FN; ++j)
         b_frag[j] = kA + (4 * lh) * BN + (((wave_n * T::kWaveN + 32 * j) ^ (32 * lh)) + li);
 
+    float (*stage)[kStage] = lds[group];   // this group's ring of S buffers
+
     const int total = g.tiles_m * g.tiles_n;
     for (int w = blockIdx.x; w < total; w += gridDim.x) {
         const int t = (int)gridDim.x == total ? xcd_contiguous(w, total) : w;
@@ -386,14 +400,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 #pragma unroll
             for (int j = 0; j < kLoadsA; ++j) {
                 const bool ok = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K;
-                buffer_to_lds(ra, &lds[buf][(wave * kLoadsA + j) * kSpanA], ok ? a_off[j] : kOutOfRange, 4 * kVecA);
+                buffer_to_lds(ra, &stage[buf][(gw * kLoadsA + j) * kSpanA], ok ? a_off[j] : kOutOfRange, 4 * kVecA);
             }
             const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
                 (void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0, (int)kOutOfRange, kRawBufferFlags);
 #pragma unroll
             for (int j = 0; j < kLoadsB; ++j) {
                 const bool ok = k0 + b_k[j] < g.K && n0 + b_c[j] < g.N;
-                buffer_to_lds(rb, &lds[buf][kA + (wave * kLoadsB + j) * kSpanB], ok ? b_off[j] : kOutOfRange, 4 * kVecB);
+                buffer_to_lds(rb, &stage[buf][kA + (gw * kLoadsB + j) * kSpanB], ok ? b_off[j] : kOutOfRange, 4 * kVecB);
             }
         };
 
@@ -406,51 +420,102 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.f;
 
+        // Group `group` takes panels group, group + KS, group + 2*KS, ...;
+        // round `it` is its panel it*KS + group, held in buffer it % S.
+        // Rounds it+1 .. it+S-1 are in flight while round it is computed.
         const int ktiles = (g.K + BK - 1) / BK;
-        issue(0, 0);
+        const int rounds = (ktiles + KS - 1) / KS;
+        auto exists = [&](int it) { return it < rounds && (KS == 1 || it * KS + group < ktiles); };
+#pragma unroll
+        for (int it = 0; it < S - 1; ++it)
+            if (exists(it))
+                issue(it, (it * KS + group) * BK);
+        for (int it = 0; it < rounds; ++it) {
+            // Round it has landed once no more than the loads of the rounds
+            // after it (up to S-2 of them, kLoads each) are outstanding; the
+            // LDS reads of round it-1 are complete as well.  Then the barrier
+            // makes every wave's panel visible and frees buffer (it-1) % S.
+            if (S > 2 && exists(it + S - 2))
+                asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * kLoads) : "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            if (exists(it + S - 1))
+                issue((it + S - 1) % S, ((it + S - 1) * KS + group) * BK);
+            if (exists(it)) {
+                const float *pa = stage[it % S] + a_frag;
+                const float *pb = stage[it % S];
+#pragma unroll
+                for (int q = 0; q < BK / 8; ++q) {
+                    f32x4 a[FM];
+                    float b[4][FN];
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+                        a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz));
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
+#pragma unroll
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j)
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+        // Every wave is done with the panel buffers before they are reused
+        // (by the K-split reduction, or by the next tile's first loads).
         __syncthreads();
-        for (int kt = 0; kt < ktiles; ++kt) {
-            const int cur = kt & 1;
-            // Buffer cur^1 was last read before the previous barrier.
-            if (kt + 1 < ktiles)
-                issue(cur ^ 1, (kt + 1) * BK);
-            const float *pa = lds[cur] + a_frag;
-            const float *pb = lds[cur];
-#pragma unroll
-            for (int q = 0; q < BK / 8; ++q) {
-                f32x4 a[FM];
-                float b[4][FN];
-#pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz));
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int j = 0; j < FN; ++j)
-                        b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
+
+        if (KS > 1) {
+            // Fold the groups' partial sums into group 0 in a fixed order
+            // (group 1, then 2, ...), through LDS laid out as C's tile.  The
+            // panel buffers are free: the loop ended with a barrier.
+            float *red = &lds[0][0][0];
+            for (int src = 1; src < KS; ++src) {
+                if (group == src) {
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
                         for (int j = 0; j < FN; ++j)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int row = wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                                red[row * BN + wave_n * T::kWaveN + j * 32 + li] = acc[i][j][r];
+                            }
+                }
+                __syncthreads();
+                if (group == 0) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int row = wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                                acc[i][j][r] += red[row * BN + wave_n * T::kWaveN + j * 32 + li];
+                            }
+                }
+                __syncthreads();
             }
-            // Waits for this wave's loads of the next panel and its reads of
-            // this one, then for every other wave.
-            __syncthreads();
         }
 
+        if (group == 0) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) {
+            for (int i = 0; i < FM; ++i) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
+                for (int j = 0; j < FN; ++j) {
+                    const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                    if (row < g.M && col < g.N)
-                        g.C[(int64_t)row * g.ldc + col] = acc[i][j][r];
+                    for (int r = 0; r < 16; ++r) {
+                        const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                        if (row < g.M && col < g.N)
+                            g.C[(int64_t)row * g.ldc + col] = acc[i][j][r];
+                    }
                 }
             }
         }
@@ -543,6 +608,14 @@ using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;   // 4 waves of 64 x 64
 using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;     // 4 waves of 64 x 32
 using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;     // 4 waves of 32 x 64
 using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;       // 4 waves of 32 x 32
+using Tile64x64S4 = MfmaTile<64, 64, 16, 2, 2, 4>;   // 4 K-split groups of 4 waves
+using Tile64x64S2 = MfmaTile<64, 64, 16, 2, 2, 2>;
+using Tile64x128S2 = MfmaTile<64, 128, 16, 2, 2, 2>;
+using Tile128x128S2 = MfmaTile<128, 128, 16, 2, 2, 2>;
+using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;     // 3-buffer ring
+using Tile64x64S4R3 = MfmaTile<64, 64, 16, 2, 2, 4, 3>;
+using Tile64x64S4R4 = MfmaTile<64, 64, 16, 2, 2, 4, 4>;
+using Tile256x256R3 = MfmaTile<256, 256, 16, 2, 4, 1, 3>;
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -556,6 +629,14 @@ enum ConfigId {
     kCfgStaged256x256,
     kCfgStaged128x128,
     kCfgStaged64x64,
+    kCfgDma64x64S4,
+    kCfgDma64x64S2,
+    kCfgDma64x128S2,
+    kCfgDma128x128S2,
+    kCfgDma128x128R3,
+    kCfgDma64x64S4R3,
+    kCfgDma64x64S4R4,
+    kCfgDma256x256R3,
     kNumConfigs
 };
 
@@ -577,6 +658,14 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     {"staged_256x256x16", 256, 256, Tile256x256::kThreads, false},
     {"staged_128x128x16", 128, 128, Tile128x128::kThreads, false},
     {"staged_64x64x16", 64, 64, Tile64x64::kThreads, false},
+    {"dma_64x64x16_ksplit4", 64, 64, Tile64x64S4::kThreads, true},
+    {"dma_64x64x16_ksplit2", 64, 64, Tile64x64S2::kThreads, true},
+    {"dma_64x128x16_ksplit2", 64, 128, Tile64x128S2::kThreads, true},
+    {"dma_128x128x16_ksplit2", 128, 128, Tile128x128S2::kThreads, true},
+    {"dma_128x128x16_ring3", 128, 128, Tile128x128R3::kThreads, true},
+    {"dma_64x64x16_ksplit4_ring3", 64, 64, Tile64x64S4R3::kThreads, true},
+    {"dma_64x64x16_ksplit4_ring4", 64, 64, Tile64x64S4R4::kThreads, true},
+    {"dma_256x256x16_ring3", 256, 256, Tile256x256R3::kThreads, true},
 };
 
 template <class T, template <class, bool, bool> class Kernel>
@@ -632,14 +721,19 @@ bool dma_offsets_fit(int bm, int bn, int64_t lda, int64_t ldb)
 
 // Tile choice by shape, from the configuration sweep (sweep.py) on MI355X.
 // Output tiles are the unit of parallelism and a compute unit needs several
-// waves per SIMD to keep its matrix cores fed, so the rule is: 128 x 128
-// tiles when there are at least four per compute unit (256 CUs), else 64-row
-// or 64-column tiles if there are at least two per CU, else 64 x 64.
+// waves per SIMD to keep its matrix cores fed:
+//  * at least four 128 x 128 tiles per CU (256 CUs): 128 x 128, with a
+//    three-buffer panel ring when K is short (the loads of the first panels
+//    are then a large part of each tile's time);
+//  * fewer than two 64 x 64 tiles per CU with a long K (the skinny shapes):
+//    64 x 64 with the K range split over four wave groups inside the
+//    workgroup, so every CU still runs 16 waves;
+//  * otherwise 64-row or 64-column tiles if there are at least two per CU,
+//    else 64 x 64.
 // Problems with fewer than 16 rows or columns use the vector-FMA kernel,
 // where a 32-wide matrix-core block would be mostly padding.
 int select_config(int M, int N, int K, bool dma_ok)
 {
-    (void)K;
     if (M < 16 || N < 16)
         return kCfgValu64;
     auto tiles = [&](int c) { return ceil_div(M, kConfigs[c].bm) * ceil_div(N, kConfigs[c].bn); };
@@ -649,7 +743,9 @@ int select_config(int M, int N, int K, bool dma_ok)
         return kCfgStaged64x64;
     }
     if (tiles(kCfgDma128x128) >= 4 * kComputeUnits)
-        return kCfgDma128x128;
+        return K <= 512 ? kCfgDma128x128R3 : kCfgDma128x128;
+    if (tiles(kCfgDma64x64) < 2 * kComputeUnits && K >= 2048)
+        return kCfgDma64x64S4;
     const int wide = N >= M ? kCfgDma64x128 : kCfgDma128x64;
     if (tiles(wide) >= 2 * kComputeUnits)
         return wide;
@@ -750,6 +846,14 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     case kCfgStaged256x256: err = launch_mfma<Tile256x256>(g, va, vb, p.grid, stream); break;
     case kCfgStaged128x128: err = launch_mfma<Tile128x128>(g, va, vb, p.grid, stream); break;
     case kCfgStaged64x64: err = launch_mfma<Tile64x64>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x64S4: err = launch_dma<Tile64x64S4>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x64S2: err = launch_dma<Tile64x64S2>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x128S2: err = launch_dma<Tile64x128S2>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x128S2: err = launch_dma<Tile128x128S2>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x128R3: err = launch_dma<Tile128x128R3>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x64S4R3: err = launch_dma<Tile64x64S4R3>(g, va, vb, p.grid, stream); break;
+    case kCfgDma64x64S4R4: err = launch_dma<Tile64x64S4R4>(g, va, vb, p.grid, stream); break;
+    case kCfgDma256x256R3: err = launch_dma<Tile256x256R3>(g, va, vb, p.grid, stream); break;
     default: return GEMM_F32_ERR_CONFIG;
     }
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;

@@ -129,7 +129,9 @@ def test_wide_rows_fall_back_to_staged_kernels():
 
 
 @pytest.mark.parametrize("shape,name", [
-    ((8192, 8192, 8192), "dma_128x128"), ((2048, 2048, 2048), "dma_64x128"),
+    ((8192, 8192, 8192), "dma_128x128x16 "), ((2048, 2048, 2048), "dma_64x128"),
+    ((8192, 8192, 128), "dma_128x128x16_ring3"), ((16384, 64, 4096), "dma_64x64x16_ksplit4"),
+    ((64, 16384, 4096), "dma_64x64x16_ksplit4"),
     ((1000, 1000, 1000), "dma_64x64"), ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
 ])
 def test_selection(shape, name):
