@@ -10,7 +10,8 @@ Timing follows the pages' method: W untimed warm-ups, then K timed calls with
 a device synchronisation on both sides; HIP events around each call on the
 stream it is enqueued on give the per-launch kernel time used for the
 roofline.  ``--table`` also times the 2048^3 case and every other workload
-shape (on stderr).  The last stdout line is one JSON object.
+shape (on stderr; their warm-up also runs for at least 0.2 s, since those
+kernels are short).  The last stdout line is one JSON object.
 """
 from __future__ import annotations
 
@@ -40,8 +41,13 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1):
-    """Returns a dict of timings for one shape (inputs generated and copied first)."""
+def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1, min_warm_s=0.0):
+    """Returns a dict of timings for one shape (inputs generated and copied first).
+
+    Warm-up is `warmup` calls, continued (in groups of 10) until at least
+    `min_warm_s` seconds of calls have run when that is non-zero, so that a
+    short kernel is not timed while the GPU clock is still ramping up after
+    the idle time spent generating its inputs."""
     from dense_fp32_gemm_amd import inputs
     A, B = inputs.uniform(M, N, K)
     dev = torch.device("cuda:0")
@@ -58,9 +64,13 @@ def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1):
         if rc != gb.GEMM_F32_OK:
             raise gb.GemmError(rc)
 
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done = 0
+    while done < warmup or (min_warm_s and time.perf_counter() - t0 < min_warm_s):
+        for _ in range(1 if done < warmup else 10):
+            call()
+            done += 1
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -170,7 +180,7 @@ def main():
         for shp in TABLE:
             if tuple(shp) == (M, N, K):
                 continue
-            r = time_gemm(torch, gb, *shp, args.steps, args.warmup, args.config)
+            r = time_gemm(torch, gb, *shp, args.steps, args.warmup, args.config, min_warm_s=0.2)
             extra["x".join(map(str, shp))] = round(r["tflops_event_mean"], 3)
             log(f"{r['M']:>6} {r['N']:>6} {r['K']:>6}  {r['event_ms_mean']*1e3:10.1f} us  "
                 f"{r['tflops_event_mean']:8.2f} TFLOPS  {r['gbs_event_mean']:8.1f} GB/s  {r['kernel']}")

@@ -329,12 +329,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int kVecA = VEC_A ? 4 : 1, kVecB = VEC_B ? 4 : 1;
     constexpr int kSpanA = kWaveSize * kVecA;         // floats one instruction moves
     constexpr int kSpanB = kWaveSize * kVecB;
-    constexpr int kLoadsA = kA / kSpanA / NW;         // instructions per wave per panel
-    constexpr int kLoadsB = kB / kSpanB / NW;
-    static_assert(kA % (kSpanA * NW) == 0 && kB % (kSpanB * NW) == 0, "panel split");
+    // Load instructions per panel, dealt to the group's waves in order; when
+    // a panel has fewer instructions than NW times the per-wave count, the
+    // last waves skip the missing ones.
+    constexpr int kInstA = kA / kSpanA, kInstB = kB / kSpanB;
+    constexpr int kLoadsA = (kInstA + NW - 1) / NW;   // instructions per wave per panel
+    constexpr int kLoadsB = (kInstB + NW - 1) / NW;
+    constexpr bool kEvenA = kInstA % NW == 0, kEvenB = kInstB % NW == 0;
+    static_assert(kA % kSpanA == 0 && kB % kSpanB == 0, "panel split");
     constexpr int S = T::kStages;
     constexpr int kLoads = kLoadsA + kLoadsB;         // per wave per round
     static_assert(S >= 2 && (S - 2) * kLoads <= 63, "vmcnt range");
+    static_assert(S == 2 || (kEvenA && kEvenB), "partial vmcnt waits need equal per-wave load counts");
     static_assert(KS * S * kStage * 4 <= 160 * 1024, "LDS budget");
     static_assert(KS == 1 || KS * S * kStage >= BM * BN, "the K-split reduction reuses the panel buffers");
     // Each K-split group owns S panel buffers, used as a ring.
@@ -399,6 +405,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 (void *)(g.A + ((int64_t)m0 * g.lda + k0)), 0, (int)kOutOfRange, kRawBufferFlags);
 #pragma unroll
             for (int j = 0; j < kLoadsA; ++j) {
+                if (!kEvenA && gw * kLoadsA + j >= kInstA)
+                    break;
                 const bool ok = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K;
                 buffer_to_lds(ra, &stage[buf][(gw * kLoadsA + j) * kSpanA], ok ? a_off[j] : kOutOfRange, 4 * kVecA);
             }
@@ -406,6 +414,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 (void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0, (int)kOutOfRange, kRawBufferFlags);
 #pragma unroll
             for (int j = 0; j < kLoadsB; ++j) {
+                if (!kEvenB && gw * kLoadsB + j >= kInstB)
+                    break;
                 const bool ok = k0 + b_k[j] < g.K && n0 + b_c[j] < g.N;
                 buffer_to_lds(rb, &stage[buf][kA + (gw * kLoadsB + j) * kSpanB], ok ? b_off[j] : kOutOfRange, 4 * kVecB);
             }
@@ -601,42 +611,32 @@ __global__ __launch_bounds__(256) void fill_zero(float *C, int64_t ldc, int M, i
 // ---------------------------------------------------------------------------
 // Configurations
 // ---------------------------------------------------------------------------
-using Tile256x256 = MfmaTile<256, 256, 16, 2, 4>;   // 8 waves of 128 x 64
-using Tile256x128 = MfmaTile<256, 128, 16, 2, 2>;   // 4 waves of 128 x 64
-using Tile128x256 = MfmaTile<128, 256, 16, 2, 2>;   // 4 waves of 64 x 128
-using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;   // 4 waves of 64 x 64
-using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;     // 4 waves of 64 x 32
-using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;     // 4 waves of 32 x 64
-using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;       // 4 waves of 32 x 32
-using Tile64x64S4 = MfmaTile<64, 64, 16, 2, 2, 4>;   // 4 K-split groups of 4 waves
-using Tile64x64S2 = MfmaTile<64, 64, 16, 2, 2, 2>;
-using Tile64x128S2 = MfmaTile<64, 128, 16, 2, 2, 2>;
-using Tile128x128S2 = MfmaTile<128, 128, 16, 2, 2, 2>;
-using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;     // 3-buffer ring
+// Tile shapes: BM x BN output tile, BK = 16 panel depth, WAVES_M x WAVES_N
+// waves each owning a (BM/WAVES_M) x (BN/WAVES_N) block; optional K-split
+// groups and panel-ring depth.
+using Tile256x256W16 = MfmaTile<256, 256, 16, 4, 4>;    // 16 waves of 64 x 64
+using Tile128x128W16 = MfmaTile<128, 128, 16, 4, 4>;    // 16 waves of 32 x 32
+using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;       // 4 waves of 64 x 64
+using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;         // 4 waves of 64 x 32
+using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;         // 4 waves of 32 x 64
+using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;           // 4 waves of 32 x 32
+using Tile64x64S4 = MfmaTile<64, 64, 16, 2, 2, 4>;      // 4 K-split groups of 4 waves
+using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;   // three-buffer panel ring
 using Tile64x64S4R3 = MfmaTile<64, 64, 16, 2, 2, 4, 3>;
-using Tile64x64S4R4 = MfmaTile<64, 64, 16, 2, 2, 4, 4>;
-using Tile256x256R3 = MfmaTile<256, 256, 16, 2, 4, 1, 3>;
 
 enum ConfigId {
     kCfgValu64 = 0,
-    kCfgDma256x256,
-    kCfgDma256x128,
-    kCfgDma128x256,
+    kCfgDma256x256W16,
+    kCfgDma128x128W16,
     kCfgDma128x128,
     kCfgDma128x64,
     kCfgDma64x128,
     kCfgDma64x64,
-    kCfgStaged256x256,
-    kCfgStaged128x128,
-    kCfgStaged64x64,
     kCfgDma64x64S4,
-    kCfgDma64x64S2,
-    kCfgDma64x128S2,
-    kCfgDma128x128S2,
     kCfgDma128x128R3,
     kCfgDma64x64S4R3,
-    kCfgDma64x64S4R4,
-    kCfgDma256x256R3,
+    kCfgStaged128x128,
+    kCfgStaged64x64,
     kNumConfigs
 };
 
@@ -648,24 +648,17 @@ struct ConfigInfo {
 
 const ConfigInfo kConfigs[kNumConfigs] = {
     {"valu_64x64", kValuTile, kValuTile, kValuThreads, false},
-    {"dma_256x256x16", 256, 256, Tile256x256::kThreads, true},
-    {"dma_256x128x16", 256, 128, Tile256x128::kThreads, true},
-    {"dma_128x256x16", 128, 256, Tile128x256::kThreads, true},
+    {"dma_256x256x16_w16", 256, 256, Tile256x256W16::kThreads, true},
+    {"dma_128x128x16_w16", 128, 128, Tile128x128W16::kThreads, true},
     {"dma_128x128x16", 128, 128, Tile128x128::kThreads, true},
     {"dma_128x64x16", 128, 64, Tile128x64::kThreads, true},
     {"dma_64x128x16", 64, 128, Tile64x128::kThreads, true},
     {"dma_64x64x16", 64, 64, Tile64x64::kThreads, true},
-    {"staged_256x256x16", 256, 256, Tile256x256::kThreads, false},
-    {"staged_128x128x16", 128, 128, Tile128x128::kThreads, false},
-    {"staged_64x64x16", 64, 64, Tile64x64::kThreads, false},
     {"dma_64x64x16_ksplit4", 64, 64, Tile64x64S4::kThreads, true},
-    {"dma_64x64x16_ksplit2", 64, 64, Tile64x64S2::kThreads, true},
-    {"dma_64x128x16_ksplit2", 64, 128, Tile64x128S2::kThreads, true},
-    {"dma_128x128x16_ksplit2", 128, 128, Tile128x128S2::kThreads, true},
     {"dma_128x128x16_ring3", 128, 128, Tile128x128R3::kThreads, true},
     {"dma_64x64x16_ksplit4_ring3", 64, 64, Tile64x64S4R3::kThreads, true},
-    {"dma_64x64x16_ksplit4_ring4", 64, 64, Tile64x64S4R4::kThreads, true},
-    {"dma_256x256x16_ring3", 256, 256, Tile256x256R3::kThreads, true},
+    {"staged_128x128x16", 128, 128, Tile128x128::kThreads, false},
+    {"staged_64x64x16", 64, 64, Tile64x64::kThreads, false},
 };
 
 template <class T, template <class, bool, bool> class Kernel>
@@ -720,14 +713,15 @@ bool dma_offsets_fit(int bm, int bn, int64_t lda, int64_t ldb)
 }
 
 // Tile choice by shape, from the configuration sweep (sweep.py) on MI355X.
-// Output tiles are the unit of parallelism and a compute unit needs several
-// waves per SIMD to keep its matrix cores fed:
-//  * at least four 128 x 128 tiles per CU (256 CUs): 128 x 128, with a
-//    three-buffer panel ring when K is short (the loads of the first panels
-//    are then a large part of each tile's time);
-//  * fewer than two 64 x 64 tiles per CU with a long K (the skinny shapes):
-//    64 x 64 with the K range split over four wave groups inside the
-//    workgroup, so every CU still runs 16 waves;
+// Output tiles are the unit of parallelism, and a compute unit needs several
+// waves per SIMD to keep its matrix cores fed, so the rule prefers big tiles
+// with 16 waves when there are enough of them (256 compute units):
+//  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 16 waves
+//    (short K: the per-tile start-up and the C store weigh more than reuse);
+//  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64;
+//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
+//  * fewer than two 64 x 64 tiles per CU with K >= 2048 (skinny shapes):
+//    64 x 64 with K split over four wave groups inside the workgroup;
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // Problems with fewer than 16 rows or columns use the vector-FMA kernel,
@@ -742,8 +736,12 @@ int select_config(int M, int N, int K, bool dma_ok)
             return kCfgStaged128x128;
         return kCfgStaged64x64;
     }
-    if (tiles(kCfgDma128x128) >= 4 * kComputeUnits)
-        return K <= 512 ? kCfgDma128x128R3 : kCfgDma128x128;
+    if (K <= 512 && tiles(kCfgDma128x128W16) >= 4 * kComputeUnits)
+        return kCfgDma128x128W16;
+    if (tiles(kCfgDma256x256W16) >= kComputeUnits)
+        return kCfgDma256x256W16;
+    if (tiles(kCfgDma128x128W16) >= kComputeUnits)
+        return kCfgDma128x128W16;
     if (tiles(kCfgDma64x64) < 2 * kComputeUnits && K >= 2048)
         return kCfgDma64x64S4;
     const int wide = N >= M ? kCfgDma64x128 : kCfgDma128x64;
@@ -836,24 +834,17 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
         gemm_f32_valu<<<p.grid, kValuThreads, 0, stream>>>(g);
         err = hipGetLastError();
         break;
-    case kCfgDma256x256: err = launch_dma<Tile256x256>(g, va, vb, p.grid, stream); break;
-    case kCfgDma256x128: err = launch_dma<Tile256x128>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x256: err = launch_dma<Tile128x256>(g, va, vb, p.grid, stream); break;
+    case kCfgDma256x256W16: err = launch_dma<Tile256x256W16>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x128W16: err = launch_dma<Tile128x128W16>(g, va, vb, p.grid, stream); break;
     case kCfgDma128x128: err = launch_dma<Tile128x128>(g, va, vb, p.grid, stream); break;
     case kCfgDma128x64: err = launch_dma<Tile128x64>(g, va, vb, p.grid, stream); break;
     case kCfgDma64x128: err = launch_dma<Tile64x128>(g, va, vb, p.grid, stream); break;
     case kCfgDma64x64: err = launch_dma<Tile64x64>(g, va, vb, p.grid, stream); break;
-    case kCfgStaged256x256: err = launch_mfma<Tile256x256>(g, va, vb, p.grid, stream); break;
-    case kCfgStaged128x128: err = launch_mfma<Tile128x128>(g, va, vb, p.grid, stream); break;
-    case kCfgStaged64x64: err = launch_mfma<Tile64x64>(g, va, vb, p.grid, stream); break;
     case kCfgDma64x64S4: err = launch_dma<Tile64x64S4>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x64S2: err = launch_dma<Tile64x64S2>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x128S2: err = launch_dma<Tile64x128S2>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x128S2: err = launch_dma<Tile128x128S2>(g, va, vb, p.grid, stream); break;
     case kCfgDma128x128R3: err = launch_dma<Tile128x128R3>(g, va, vb, p.grid, stream); break;
     case kCfgDma64x64S4R3: err = launch_dma<Tile64x64S4R3>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x64S4R4: err = launch_dma<Tile64x64S4R4>(g, va, vb, p.grid, stream); break;
-    case kCfgDma256x256R3: err = launch_dma<Tile256x256R3>(g, va, vb, p.grid, stream); break;
+    case kCfgStaged128x128: err = launch_mfma<Tile128x128>(g, va, vb, p.grid, stream); break;
+    case kCfgStaged64x64: err = launch_mfma<Tile64x64>(g, va, vb, p.grid, stream); break;
     default: return GEMM_F32_ERR_CONFIG;
     }
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;

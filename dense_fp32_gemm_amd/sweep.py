@@ -8,8 +8,8 @@ some) first runs on quarter-step operands, whose product is exact in binary32
 and therefore identical bit for bit whatever the summation order: each
 configuration's C must equal the first configuration's C, otherwise it is
 reported as failing and not timed.  Configurations that pass are then timed
-on uniform[-1,1) operands (hipEvents around each call, after warm-up) and
-ranked by mean time.  This is how the shape -> configuration table in
+on uniform[-1,1) operands (hipEvents around each call, after at least
+--warmup calls and 0.2 s of warm-up) and ranked by mean time.  This is how the shape -> configuration table in
 gemm_f32.hip is chosen; the Lecture 12 final-project page's sweep.cu follows
 the same "correct first, then fast" order for its block/tile/coarsening
 search.
@@ -19,6 +19,7 @@ from __future__ import annotations
 import argparse
 import csv
 import sys
+import time
 
 import numpy as np
 
@@ -74,8 +75,15 @@ def sweep_shape(torch, shape, configs, steps, warmup, log=print):
     flop = 2.0 * M * N * K
     nbytes = 4.0 * (M * K + K * N + M * N)
     for c in passed:
-        for _ in range(warmup):
-            _run(torch, c, A, B, C, stream)
+        # At least `warmup` calls and 0.2 s of them: short kernels must not be
+        # timed while the clock is still ramping up.
+        t0 = time.perf_counter()
+        done = 0
+        while done < warmup or time.perf_counter() - t0 < 0.2:
+            for _ in range(1 if done < warmup else 10):
+                _run(torch, c, A, B, C, stream)
+                done += 1
+            torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
         torch.cuda.synchronize()

@@ -238,3 +238,36 @@ def test_runs_on_a_side_stream_and_repeats_bit_identically(dev):
     s.synchronize()
     assert torch.equal(c1, c2)
     assert_close(c1.cpu().numpy(), oracle.gemm(A, B), "side stream")
+
+
+def test_graph_capture_replays_match_eager(dev):
+    """gemm_f32 enqueues plain kernel launches (no memset, no allocation), so
+    it can be captured into a HIP graph; every replay must reproduce the
+    eager result bit for bit (K = 0 included: its fill is a kernel too)."""
+    A, B = operands("uniform", 1000, 1000, 1000)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    eager = gb.matmul(dA, dB)
+    z = torch.empty((0, 64), dtype=torch.float32, device=dev)
+    zb = torch.empty((64, 0), dtype=torch.float32, device=dev)
+    out = torch.full((1000, 1000), float("nan"), device=dev)
+    zout = torch.full((64, 64), float("nan"), device=dev)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        gb.matmul(dA, dB, out=out)          # warm-up on the capture stream
+        gb.matmul(zb, z, out=zout)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=s):
+        gb.matmul(dA, dB, out=out)
+        gb.matmul(zb, z, out=zout)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        zout.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        assert torch.equal(zout, torch.zeros_like(zout))
