@@ -290,11 +290,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 // outside the resource's range reads as zero, so ragged rows, columns and
 // K-tails are zero-filled by pointing their lanes at an out-of-range offset.
 //
-// LDS layouts (per panel, BK = 16):
-//  * A: [BM][16] floats, the four 16-byte chunks of row r permuted by
-//    chunk ^ swz_a(r).  A half-wave's 128-bit fragment reads (32 rows, one
-//    chunk) then touch every bank exactly once.
-//  * B: [16][BN] floats; in rows with bit 2 of k set, columns are stored at
+// LDS layouts (per panel, BK = 16 or 32):
+//  * A: [BM][BK] floats, the BK/4 16-byte chunks of row r permuted by
+//    chunk ^ swz_a<BK>(r).  A half-wave's 128-bit fragment reads (32 rows,
+//    one chunk) then touch every bank exactly once.
+//  * B: [BK][BN] floats; in rows with bit 2 of k set, columns are stored at
 //    col ^ 32.  The two lane halves read rows k and k+4 (same columns), which
 //    the swap moves onto different banks.
 // Buffer resources are rebased on every panel (A at row m0 / column k0, B at
@@ -303,7 +303,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as 0
 constexpr int kRawBufferFlags = 0x00020000;      // dword 3 of a raw buffer resource
 
-__device__ inline int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// Chunk permutation of A-panel row r (BK/4 chunks of 16 bytes per row).
+template <int BK>
+__device__ inline int swz_a(int r)
+{
+    static_assert(BK == 16 || BK == 32, "A-panel swizzles exist for 16- and 32-deep panels");
+    return BK == 16 ? ((r >> 1) ^ (r >> 3)) & 3 : (r ^ (r >> 3)) & 7;
+}
 
 __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_base, uint32_t offset, int bytes)
 {
@@ -321,7 +327,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int NW = T::kGroupWaves;                // waves per K-split group
     constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
-    static_assert(BK == 16, "the A layout permutes four 16-byte chunks per row");
+    static_assert(BK == 16 || BK == 32, "the A layout permutes the 16-byte chunks of 16- or 32-deep rows");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
     constexpr int kA = BM * BK;                       // floats per A panel
     constexpr int kB = BK * BN;                       // floats per B panel
@@ -363,7 +369,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     for (int j = 0; j < kLoadsA; ++j) {
         const int f = (gw * kLoadsA + j) * kSpanA + lane * kVecA;   // LDS slot (float index)
         const int r = f / BK, e = f % BK;
-        const int k = 4 * ((e / 4) ^ swz_a(r)) + e % 4;
+        const int k = 4 * ((e / 4) ^ swz_a<BK>(r)) + e % 4;
         a_r[j] = r;
         a_k[j] = k;
         a_off[j] = (uint32_t)(r * g.lda + k) * 4u;
@@ -381,7 +387,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     }
     // Fragment read addresses (floats within a panel buffer).
     const int a_frag = (wave_m * T::kWaveM + li) * BK;
-    const int a_swz = swz_a(li);
+    int a_swz[FM];             // chunk permutation of each fragment's row
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+        a_swz[i] = swz_a<BK>(wave_m * T::kWaveM + i * 32 + li);
     // Column of fragment j after the half swap of rows with bit 2 of k set
     // (k = 8q + 4*lh + s, so that bit is lh); the fragment base is a multiple
     // of 32, so the swap only flips its bit 5.
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     float b[4][FN];
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
-                        a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz));
+                        a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz[i]));
 #pragma unroll
                     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -623,6 +632,8 @@ using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;           // 4 waves of 32 x 32
 using Tile64x64S4 = MfmaTile<64, 64, 16, 2, 2, 4>;      // 4 K-split groups of 4 waves
 using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;   // three-buffer panel ring
 using Tile64x64S4R3 = MfmaTile<64, 64, 16, 2, 2, 4, 3>;
+using Tile256x256K32W16 = MfmaTile<256, 256, 32, 4, 4>;  // 32-deep panels
+using Tile128x128K32W16 = MfmaTile<128, 128, 32, 4, 4>;
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -637,28 +648,32 @@ enum ConfigId {
     kCfgDma64x64S4R3,
     kCfgStaged128x128,
     kCfgStaged64x64,
+    kCfgDma256x256K32W16,
+    kCfgDma128x128K32W16,
     kNumConfigs
 };
 
 struct ConfigInfo {
     const char *name;
-    int bm, bn, threads;
+    int bm, bn, bk, threads;
     bool dma;
 };
 
 const ConfigInfo kConfigs[kNumConfigs] = {
-    {"valu_64x64", kValuTile, kValuTile, kValuThreads, false},
-    {"dma_256x256x16_w16", 256, 256, Tile256x256W16::kThreads, true},
-    {"dma_128x128x16_w16", 128, 128, Tile128x128W16::kThreads, true},
-    {"dma_128x128x16", 128, 128, Tile128x128::kThreads, true},
-    {"dma_128x64x16", 128, 64, Tile128x64::kThreads, true},
-    {"dma_64x128x16", 64, 128, Tile64x128::kThreads, true},
-    {"dma_64x64x16", 64, 64, Tile64x64::kThreads, true},
-    {"dma_64x64x16_ksplit4", 64, 64, Tile64x64S4::kThreads, true},
-    {"dma_128x128x16_ring3", 128, 128, Tile128x128R3::kThreads, true},
-    {"dma_64x64x16_ksplit4_ring3", 64, 64, Tile64x64S4R3::kThreads, true},
-    {"staged_128x128x16", 128, 128, Tile128x128::kThreads, false},
-    {"staged_64x64x16", 64, 64, Tile64x64::kThreads, false},
+    {"valu_64x64", kValuTile, kValuTile, 16, kValuThreads, false},
+    {"dma_256x256x16_w16", 256, 256, 16, Tile256x256W16::kThreads, true},
+    {"dma_128x128x16_w16", 128, 128, 16, Tile128x128W16::kThreads, true},
+    {"dma_128x128x16", 128, 128, 16, Tile128x128::kThreads, true},
+    {"dma_128x64x16", 128, 64, 16, Tile128x64::kThreads, true},
+    {"dma_64x128x16", 64, 128, 16, Tile64x128::kThreads, true},
+    {"dma_64x64x16", 64, 64, 16, Tile64x64::kThreads, true},
+    {"dma_64x64x16_ksplit4", 64, 64, 16, Tile64x64S4::kThreads, true},
+    {"dma_128x128x16_ring3", 128, 128, 16, Tile128x128R3::kThreads, true},
+    {"dma_64x64x16_ksplit4_ring3", 64, 64, 16, Tile64x64S4R3::kThreads, true},
+    {"staged_128x128x16", 128, 128, 16, Tile128x128::kThreads, false},
+    {"staged_64x64x16", 64, 64, 16, Tile64x64::kThreads, false},
+    {"dma_256x256x32_w16", 256, 256, 32, Tile256x256K32W16::kThreads, true},
+    {"dma_128x128x32_w16", 128, 128, 32, Tile128x128K32W16::kThreads, true},
 };
 
 template <class T, template <class, bool, bool> class Kernel>
@@ -706,20 +721,22 @@ constexpr int64_t kComputeUnits = 256;   // MI355X
 // The direct-to-LDS kernels address each panel with 32-bit buffer offsets
 // from its corner: the farthest in-range element of an A panel is
 // (BM-1)*lda + BK-1 floats away, of a B panel (BK-1)*ldb + BN-1.
-bool dma_offsets_fit(int bm, int bn, int64_t lda, int64_t ldb)
+bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 {
     const int64_t limit = (int64_t)kOutOfRange / 4;
-    return (bm - 1) * lda + 16 < limit && 15 * ldb + bn < limit;
+    return (c.bm - 1) * lda + c.bk < limit && (c.bk - 1) * ldb + c.bn < limit;
 }
 
 // Tile choice by shape, from the configuration sweep (sweep.py) on MI355X.
 // Output tiles are the unit of parallelism, and a compute unit needs several
 // waves per SIMD to keep its matrix cores fed, so the rule prefers big tiles
 // with 16 waves when there are enough of them (256 compute units):
-//  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 16 waves
-//    (short K: the per-tile start-up and the C store weigh more than reuse);
+//  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 4 waves
+//    (short K: per-tile start-up and the C store weigh more than reuse);
 //  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64;
-//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
+//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32,
+//    with 32-deep panels (each wave has few MFMAs per panel, so fewer,
+//    deeper panels halve the per-panel barrier and wait overhead);
 //  * fewer than two 64 x 64 tiles per CU with K >= 2048 (skinny shapes):
 //    64 x 64 with K split over four wave groups inside the workgroup;
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
@@ -736,12 +753,12 @@ int select_config(int M, int N, int K, bool dma_ok)
             return kCfgStaged128x128;
         return kCfgStaged64x64;
     }
-    if (K <= 512 && tiles(kCfgDma128x128W16) >= 4 * kComputeUnits)
-        return kCfgDma128x128W16;
+    if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
+        return kCfgDma128x128;
     if (tiles(kCfgDma256x256W16) >= kComputeUnits)
         return kCfgDma256x256W16;
-    if (tiles(kCfgDma128x128W16) >= kComputeUnits)
-        return kCfgDma128x128W16;
+    if (tiles(kCfgDma128x128K32W16) >= kComputeUnits)
+        return kCfgDma128x128K32W16;
     if (tiles(kCfgDma64x64) < 2 * kComputeUnits && K >= 2048)
         return kCfgDma64x64S4;
     const int wide = N >= M ? kCfgDma64x128 : kCfgDma128x64;
@@ -786,9 +803,12 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     }
     int c = config;
     if (c < 0) {
-        const bool dma_ok = dma_offsets_fit(128, 128, lda, ldb);
+        // Every direct-to-LDS configuration the rule can pick fits if the
+        // tallest A panel (256 rows) and the deepest B panel (32 rows) do.
+        const bool dma_ok = dma_offsets_fit(kConfigs[kCfgDma256x256W16], lda, ldb) &&
+                            dma_offsets_fit(kConfigs[kCfgDma128x128K32W16], lda, ldb);
         c = select_config(M, N, K, dma_ok);
-    } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c].bm, kConfigs[c].bn, lda, ldb)) {
+    } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
     const int64_t tm = ceil_div(M, kConfigs[c].bm);
@@ -845,6 +865,8 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     case kCfgDma64x64S4R3: err = launch_dma<Tile64x64S4R3>(g, va, vb, p.grid, stream); break;
     case kCfgStaged128x128: err = launch_mfma<Tile128x128>(g, va, vb, p.grid, stream); break;
     case kCfgStaged64x64: err = launch_mfma<Tile64x64>(g, va, vb, p.grid, stream); break;
+    case kCfgDma256x256K32W16: err = launch_dma<Tile256x256K32W16>(g, va, vb, p.grid, stream); break;
+    case kCfgDma128x128K32W16: err = launch_dma<Tile128x128K32W16>(g, va, vb, p.grid, stream); break;
     default: return GEMM_F32_ERR_CONFIG;
     }
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
