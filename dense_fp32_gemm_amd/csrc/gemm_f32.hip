@@ -292,8 +292,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 //
 // LDS layouts (per panel, BK = 16 or 32):
 //  * A: [BM][BK] floats, the BK/4 16-byte chunks of row r permuted by
-//    chunk ^ swz_a<BK>(r).  A half-wave's 128-bit fragment reads (32 rows,
-//    one chunk) then touch every bank exactly once.
+//    chunk ^ swz_a<BK>(r), so that the 128-bit fragment reads (32 rows, one
+//    chunk per lane half) run without bank conflicts.
 //  * B: [BK][BN] floats; in rows with bit 2 of k set, columns are stored at
 //    col ^ 32.  The two lane halves read rows k and k+4 (same columns), which
 //    the swap moves onto different banks.
@@ -304,11 +304,15 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as 0
 constexpr int kRawBufferFlags = 0x00020000;      // dword 3 of a raw buffer resource
 
 // Chunk permutation of A-panel row r (BK/4 chunks of 16 bytes per row).
+// Chosen by measurement (SQ_LDS_BANK_CONFLICT on 128-bit fragment reads of
+// 32 consecutive rows): for 64-byte rows, rows four apart share banks and
+// (r >> 2) & 3 rotates them onto different chunks, which reads with no
+// conflict cycles; for 128-byte rows (r ^ (r >> 3)) & 7 does.
 template <int BK>
 __device__ inline int swz_a(int r)
 {
     static_assert(BK == 16 || BK == 32, "A-panel swizzles exist for 16- and 32-deep panels");
-    return BK == 16 ? ((r >> 1) ^ (r >> 3)) & 3 : (r ^ (r >> 3)) & 7;
+    return BK == 16 ? (r >> 2) & 3 : (r ^ (r >> 3)) & 7;
 }
 
 __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_base, uint32_t offset, int bytes)
