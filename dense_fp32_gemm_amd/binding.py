@@ -49,6 +49,9 @@ def load() -> ctypes.CDLL:
         lib.gemm_f32_num_configs.restype = i
         lib.gemm_f32_config_name.argtypes = [i]
         lib.gemm_f32_config_name.restype = ctypes.c_char_p
+        ip = ctypes.POINTER(ctypes.c_int)
+        lib.gemm_f32_config_info.argtypes = [i, ip, ip, ip, ip, ip]
+        lib.gemm_f32_config_info.restype = i
         lib.gemm_f32_describe.argtypes = [i, i, i, i, p, i, p, i, p, i, ctypes.c_char_p, i]
         lib.gemm_f32_describe.restype = i
         lib.gemm_f32_status_string.argtypes = [i]
@@ -73,6 +76,21 @@ def gemm_f32_num_configs() -> int:
 
 def gemm_f32_config_name(config: int) -> str:
     return load().gemm_f32_config_name(config).decode()
+
+
+def gemm_f32_config_info(config: int, occupancy: bool = False) -> dict:
+    """{'bm', 'bn', 'bk', 'threads'} (+ 'blocks_per_cu' if occupancy, needs a GPU)."""
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    ptrs = [ctypes.byref(v) for v in vals]
+    if not occupancy:
+        ptrs[4] = None
+    rc = load().gemm_f32_config_info(config, *ptrs)
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_config_info")
+    out = dict(bm=vals[0].value, bn=vals[1].value, bk=vals[2].value, threads=vals[3].value)
+    if occupancy:
+        out["blocks_per_cu"] = vals[4].value
+    return out
 
 
 def gemm_f32_describe(config, M, N, K, A, lda, B, ldb, C, ldc) -> tuple[int, str]:

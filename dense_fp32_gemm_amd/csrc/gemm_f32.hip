@@ -657,29 +657,6 @@ enum ConfigId {
     kNumConfigs
 };
 
-struct ConfigInfo {
-    const char *name;
-    int bm, bn, bk, threads;
-    bool dma;
-};
-
-const ConfigInfo kConfigs[kNumConfigs] = {
-    {"valu_64x64", kValuTile, kValuTile, 16, kValuThreads, false},
-    {"dma_256x256x16_w16", 256, 256, 16, Tile256x256W16::kThreads, true},
-    {"dma_128x128x16_w16", 128, 128, 16, Tile128x128W16::kThreads, true},
-    {"dma_128x128x16", 128, 128, 16, Tile128x128::kThreads, true},
-    {"dma_128x64x16", 128, 64, 16, Tile128x64::kThreads, true},
-    {"dma_64x128x16", 64, 128, 16, Tile64x128::kThreads, true},
-    {"dma_64x64x16", 64, 64, 16, Tile64x64::kThreads, true},
-    {"dma_64x64x16_ksplit4", 64, 64, 16, Tile64x64S4::kThreads, true},
-    {"dma_128x128x16_ring3", 128, 128, 16, Tile128x128R3::kThreads, true},
-    {"dma_64x64x16_ksplit4_ring3", 64, 64, 16, Tile64x64S4R3::kThreads, true},
-    {"staged_128x128x16", 128, 128, 16, Tile128x128::kThreads, false},
-    {"staged_64x64x16", 64, 64, 16, Tile64x64::kThreads, false},
-    {"dma_256x256x32_w16", 256, 256, 32, Tile256x256K32W16::kThreads, true},
-    {"dma_128x128x32_w16", 128, 128, 32, Tile128x128K32W16::kThreads, true},
-};
-
 template <class T, template <class, bool, bool> class Kernel>
 struct Launch {
     static hipError_t run(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
@@ -694,6 +671,14 @@ struct Launch {
             hipLaunchKernelGGL((Kernel<T, false, false>::fn), dim3(grid), dim3(T::kThreads), 0, s, g);
         return hipGetLastError();
     }
+    // Resident workgroups per compute unit (the 128-bit-load instance).
+    static int occupancy()
+    {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, Kernel<T, true, true>::fn, T::kThreads, 0) != hipSuccess)
+            return -1;
+        return n;
+    }
 };
 
 // Adapters so one launcher serves both matrix-core kernels.
@@ -706,17 +691,52 @@ struct DmaKernel {
     static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB>;
 };
 
-template <class T>
-hipError_t launch_dma(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
+hipError_t launch_valu(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
 {
-    return Launch<T, DmaKernel>::run(g, va, vb, grid, s);
+    gemm_f32_valu<<<grid, kValuThreads, 0, s>>>(g);
+    return hipGetLastError();
 }
 
-template <class T>
-hipError_t launch_mfma(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
+int occupancy_valu()
 {
-    return Launch<T, PlainKernel>::run(g, va, vb, grid, s);
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_f32_valu, kValuThreads, 0) != hipSuccess)
+        return -1;
+    return n;
 }
+
+struct ConfigInfo {
+    const char *name;
+    int bm, bn, bk, threads;
+    bool dma;                    // direct-to-LDS (32-bit panel offsets)
+    hipError_t (*launch)(const GemmArgs &, bool, bool, int, hipStream_t);
+    int (*occupancy)();
+};
+
+template <class T, template <class, bool, bool> class Kernel>
+constexpr ConfigInfo config(const char *name, bool dma)
+{
+    return {name, T::BM, T::BN, T::BK, T::kThreads, dma, &Launch<T, Kernel>::run,
+            &Launch<T, Kernel>::occupancy};
+}
+
+// Indexed by ConfigId.
+const ConfigInfo kConfigs[kNumConfigs] = {
+    {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu},
+    config<Tile256x256W16, DmaKernel>("dma_256x256x16_w16", true),
+    config<Tile128x128W16, DmaKernel>("dma_128x128x16_w16", true),
+    config<Tile128x128, DmaKernel>("dma_128x128x16", true),
+    config<Tile128x64, DmaKernel>("dma_128x64x16", true),
+    config<Tile64x128, DmaKernel>("dma_64x128x16", true),
+    config<Tile64x64, DmaKernel>("dma_64x64x16", true),
+    config<Tile64x64S4, DmaKernel>("dma_64x64x16_ksplit4", true),
+    config<Tile128x128R3, DmaKernel>("dma_128x128x16_ring3", true),
+    config<Tile64x64S4R3, DmaKernel>("dma_64x64x16_ksplit4_ring3", true),
+    config<Tile128x128, PlainKernel>("staged_128x128x16", false),
+    config<Tile64x64, PlainKernel>("staged_64x64x16", false),
+    config<Tile256x256K32W16, DmaKernel>("dma_256x256x32_w16", true),
+    config<Tile128x128K32W16, DmaKernel>("dma_128x128x32_w16", true),
+};
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -851,28 +871,7 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     g.K = K;
     g.tiles_m = p.tiles_m;
     g.tiles_n = p.tiles_n;
-    const bool va = p.vec_a, vb = p.vec_b;
-    hipError_t err = hipSuccess;
-    switch (p.config) {
-    case kCfgValu64:
-        gemm_f32_valu<<<p.grid, kValuThreads, 0, stream>>>(g);
-        err = hipGetLastError();
-        break;
-    case kCfgDma256x256W16: err = launch_dma<Tile256x256W16>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x128W16: err = launch_dma<Tile128x128W16>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x128: err = launch_dma<Tile128x128>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x64: err = launch_dma<Tile128x64>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x128: err = launch_dma<Tile64x128>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x64: err = launch_dma<Tile64x64>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x64S4: err = launch_dma<Tile64x64S4>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x128R3: err = launch_dma<Tile128x128R3>(g, va, vb, p.grid, stream); break;
-    case kCfgDma64x64S4R3: err = launch_dma<Tile64x64S4R3>(g, va, vb, p.grid, stream); break;
-    case kCfgStaged128x128: err = launch_mfma<Tile128x128>(g, va, vb, p.grid, stream); break;
-    case kCfgStaged64x64: err = launch_mfma<Tile64x64>(g, va, vb, p.grid, stream); break;
-    case kCfgDma256x256K32W16: err = launch_dma<Tile256x256K32W16>(g, va, vb, p.grid, stream); break;
-    case kCfgDma128x128K32W16: err = launch_dma<Tile128x128K32W16>(g, va, vb, p.grid, stream); break;
-    default: return GEMM_F32_ERR_CONFIG;
-    }
+    const hipError_t err = kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
@@ -893,6 +892,24 @@ int gemm_f32_with_config(int config, int M, int N, int K, const float *A, int ld
 }
 
 int gemm_f32_num_configs(void) { return kNumConfigs; }
+
+int gemm_f32_config_info(int config, int *bm, int *bn, int *bk, int *threads, int *blocks_per_cu)
+{
+    if (config < 0 || config >= kNumConfigs)
+        return GEMM_F32_ERR_CONFIG;
+    const ConfigInfo &c = kConfigs[config];
+    if (bm) *bm = c.bm;
+    if (bn) *bn = c.bn;
+    if (bk) *bk = c.bk;
+    if (threads) *threads = c.threads;
+    if (blocks_per_cu) {
+        const int n = kConfigs[config].occupancy();
+        if (n < 0)
+            return GEMM_F32_ERR_LAUNCH;
+        *blocks_per_cu = n;
+    }
+    return GEMM_F32_OK;
+}
 
 const char *gemm_f32_config_name(int config)
 {

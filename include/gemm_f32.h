@@ -96,6 +96,17 @@ GEMM_F32_API int gemm_f32_num_configs(void);
 GEMM_F32_API const char *gemm_f32_config_name(int config);
 
 /*
+ * Shape of a configuration: output tile bm x bn, K-panel depth bk, threads
+ * per workgroup; any output pointer may be NULL.  If blocks_per_cu is not
+ * NULL it receives how many of its workgroups one compute unit holds at once
+ * (from the HIP occupancy calculator, which needs a GPU; without one the call
+ * returns GEMM_F32_ERR_LAUNCH).  Unknown configurations return
+ * GEMM_F32_ERR_CONFIG.
+ */
+GEMM_F32_API int gemm_f32_config_info(int config, int *bm, int *bn, int *bk,
+                                      int *threads, int *blocks_per_cu);
+
+/*
  * Writes into buf (NUL-terminated, at most buflen bytes) a one-line
  * description of what gemm_f32_with_config(config, ...) would enqueue for
  * these arguments (config -1: what gemm_f32() would enqueue): the

@@ -139,3 +139,16 @@ def test_selection(shape, name):
     M, N, K = shape
     rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
     assert rc == gb.GEMM_F32_OK and text.startswith(name), text
+
+
+def test_config_info_matches_names():
+    for c, name in enumerate(gb.config_names()):
+        info = gb.gemm_f32_config_info(c)
+        tile = name.split("_")[1]                      # e.g. "256x256x16" or "64x64"
+        dims = [int(x) for x in tile.split("x")]
+        assert [info["bm"], info["bn"]] == dims[:2], name
+        if len(dims) == 3:
+            assert info["bk"] == dims[2], name
+        assert info["threads"] % 64 == 0 and 64 <= info["threads"] <= 1024
+    with pytest.raises(gb.GemmError):
+        gb.gemm_f32_config_info(gb.gemm_f32_num_configs())

@@ -1,0 +1,36 @@
+"""The configuration sweep and the scaling report on the GPU (small sizes)."""
+import pytest
+
+from dense_fp32_gemm_amd import binding as gb
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def test_every_configuration_is_resident(cuda):
+    for c in range(gb.gemm_f32_num_configs()):
+        info = gb.gemm_f32_config_info(c, occupancy=True)
+        assert info["blocks_per_cu"] >= 1, gb.gemm_f32_config_name(c)
+
+
+def test_sweep_checks_every_configuration(cuda):
+    from dense_fp32_gemm_amd import sweep
+    rows = sweep.sweep_shape(cuda, (300, 270, 77), list(range(gb.gemm_f32_num_configs())),
+                             steps=2, warmup=1, log=lambda s: None)
+    assert len(rows) == gb.gemm_f32_num_configs()
+    assert all(r["ok"] for r in rows), [r for r in rows if not r["ok"]]
+
+
+def test_report_row(cuda):
+    from dense_fp32_gemm_amd import report
+    r = report.row_for(cuda, 256, steps=2, warmup=1)
+    assert r["check"] == "bit-exact" and r["tflops"] > 0 and r["blocks_per_cu"] >= 1
+    assert abs(r["ai"] - 2.0 * 256 ** 3 / (12.0 * 256 * 256)) < 1e-9
