@@ -638,6 +638,11 @@ using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;   // three-buffer pane
 using Tile64x64S4R3 = MfmaTile<64, 64, 16, 2, 2, 4, 3>;
 using Tile256x256K32W16 = MfmaTile<256, 256, 32, 4, 4>;  // 32-deep panels
 using Tile128x128K32W16 = MfmaTile<128, 128, 32, 4, 4>;
+using Tile64x64K32 = MfmaTile<64, 64, 32, 2, 2>;
+using Tile64x64K32S4 = MfmaTile<64, 64, 32, 2, 2, 4>;
+using Tile64x128K32 = MfmaTile<64, 128, 32, 2, 2>;
+using Tile128x64K32 = MfmaTile<128, 64, 32, 2, 2>;
+using Tile128x128K32 = MfmaTile<128, 128, 32, 2, 2>;
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -654,6 +659,11 @@ enum ConfigId {
     kCfgStaged64x64,
     kCfgDma256x256K32W16,
     kCfgDma128x128K32W16,
+    kCfgDma64x64K32,
+    kCfgDma64x64K32S4,
+    kCfgDma64x128K32,
+    kCfgDma128x64K32,
+    kCfgDma128x128K32,
     kNumConfigs
 };
 
@@ -736,6 +746,11 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config<Tile64x64, PlainKernel>("staged_64x64x16", false),
     config<Tile256x256K32W16, DmaKernel>("dma_256x256x32_w16", true),
     config<Tile128x128K32W16, DmaKernel>("dma_128x128x32_w16", true),
+    config<Tile64x64K32, DmaKernel>("dma_64x64x32", true),
+    config<Tile64x64K32S4, DmaKernel>("dma_64x64x32_ksplit4", true),
+    config<Tile64x128K32, DmaKernel>("dma_64x128x32", true),
+    config<Tile128x64K32, DmaKernel>("dma_128x64x32", true),
+    config<Tile128x128K32, DmaKernel>("dma_128x128x32", true),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -758,15 +773,16 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 4 waves
 //    (short K: per-tile start-up and the C store weigh more than reuse);
 //  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64;
-//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32,
-//    with 32-deep panels (each wave has few MFMAs per panel, so fewer,
-//    deeper panels halve the per-panel barrier and wait overhead);
+//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
 //  * fewer than two 64 x 64 tiles per CU with K >= 2048 (skinny shapes):
 //    64 x 64 with K split over four wave groups inside the workgroup;
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
-// Problems with fewer than 16 rows or columns use the vector-FMA kernel,
-// where a 32-wide matrix-core block would be mostly padding.
+// Below the two largest tiles every choice uses 32-deep K-panels: those
+// tiles give each wave few MFMAs per panel, so halving the number of panels
+// halves the per-panel barrier, wait and LDS-latency cost.  Problems with
+// fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
+// matrix-core block would be mostly padding.
 int select_config(int M, int N, int K, bool dma_ok)
 {
     if (M < 16 || N < 16)
@@ -783,12 +799,12 @@ int select_config(int M, int N, int K, bool dma_ok)
         return kCfgDma256x256W16;
     if (tiles(kCfgDma128x128K32W16) >= kComputeUnits)
         return kCfgDma128x128K32W16;
-    if (tiles(kCfgDma64x64) < 2 * kComputeUnits && K >= 2048)
-        return kCfgDma64x64S4;
-    const int wide = N >= M ? kCfgDma64x128 : kCfgDma128x64;
+    if (tiles(kCfgDma64x64K32) < 2 * kComputeUnits && K >= 2048)
+        return kCfgDma64x64K32S4;
+    const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * kComputeUnits)
         return wide;
-    return kCfgDma64x64;
+    return kCfgDma64x64K32;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

@@ -131,9 +131,9 @@ def test_wide_rows_fall_back_to_staged_kernels():
 @pytest.mark.parametrize("shape,name", [
     ((8192, 8192, 8192), "dma_256x256x16_w16 "), ((2048, 2048, 2048), "dma_128x128x32_w16 "),
     ((4096, 4096, 16384), "dma_256x256x16_w16 "), ((1024, 8192, 8192), "dma_128x128x32_w16 "),
-    ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x16_ksplit4"),
-    ((64, 16384, 4096), "dma_64x64x16_ksplit4"),
-    ((1000, 1000, 1000), "dma_64x64"), ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
+    ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
+    ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
+    ((1000, 1000, 1000), "dma_64x64x32 "), ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
 ])
 def test_selection(shape, name):
     M, N, K = shape
