@@ -271,3 +271,52 @@ def test_graph_capture_replays_match_eager(dev):
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
         assert torch.equal(zout, torch.zeros_like(zout))
+
+
+def test_long_k_quarter_step_bit_exact(dev):
+    """K = 2^20 - 16, the longest K for which quarter-step sums stay exact in
+    binary32 (|partial sums| < 2^20 at 1/16 resolution), on the skinny path."""
+    M, N, K = 64, 64, (1 << 20) - 16
+    A, B = inputs.quarter_step(M, N, K)
+    got, _ = gpu_gemm(A, B, -1, dev)
+    assert_bit_exact(got, oracle.gemm(A, B), "long K")
+
+
+def test_more_tiles_than_one_launch_holds(dev):
+    """More than 2^20 output tiles: the grid is capped and each workgroup walks
+    several tiles.  Checked on seeded samples plus the last rows (the tiles
+    the second pass of the tile loop covers), gathered on the GPU."""
+    M, N, K = 65536 + 64, 65536, 16
+    cfg = gb.config_names().index("dma_64x64x16")
+    A, B = inputs.uniform(M, N, K)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev)
+    say(f"gemm_f32 config={cfg} M={M} N={N} K={K} (tile loop)")
+    rc = gb.gemm_f32_with_config(cfg, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N,
+                                 dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    assert rc == gb.GEMM_F32_OK
+    rc, desc = gb.gemm_f32_describe(cfg, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), N)
+    assert "grid=1048576" in desc and "tiles=1025x1024" in desc, desc
+    torch.cuda.synchronize()
+    r, c = inputs.sample_positions(M, N)
+    r = np.concatenate([r, np.full(64, M - 1), np.arange(M - 64, M)])
+    c = np.concatenate([c, np.arange(0, N, N // 64), np.full(64, N - 1)])
+    got = dC[torch.from_numpy(r).to(dev), torch.from_numpy(c).to(dev)].cpu().numpy()
+    assert_close(got, oracle.gemm_at(A, B, r, c), "tile loop samples")
+    assert bool(torch.isfinite(dC).all())
+    del dC
+
+
+def test_random_shapes_layouts_and_configs(dev):
+    """Seeded fuzz: random small shapes, leading-dimension padding and base
+    offsets, each on a random configuration, bit-exact on quarter-step."""
+    rng = np.random.default_rng(20250612)
+    for trial in range(40):
+        M, N, K = (int(x) for x in rng.integers(1, 300, size=3))
+        config = int(rng.integers(-1, gb.gemm_f32_num_configs()))
+        pad = tuple(int(x) for x in rng.integers(0, 9, size=3))
+        off = tuple(int(x) for x in rng.integers(0, 4, size=3))
+        A, B = inputs.quarter_step(M, N, K, 11 + trial, 13 + trial)
+        got, _ = gpu_gemm(A, B, config, dev, pad=pad, offset=off)
+        assert_bit_exact(got, oracle.gemm(A, B), f"trial {trial}: {(M, N, K)} config {config} pad {pad} off {off}")
