@@ -443,12 +443,40 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.f;
 
+        // One k-group (8 k) of MFMA operands: A rows and B columns of this
+        // wave's 32 x 32 blocks.
+        struct Frag {
+            f32x4 a[FM];
+            float b[4][FN];
+        };
+        auto read_frag = [&](Frag &f, int buf, int q) {
+            const float *pa = stage[buf] + a_frag;
+            const float *pb = stage[buf];
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+                f.a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz[i]));
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                    f.b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
+        };
+        auto mma = [&](const Frag &f) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[s][j], acc[i][j], 0, 0, 0);
+        };
+
         // Group `group` takes panels group, group + KS, group + 2*KS, ...;
         // round `it` is its panel it*KS + group, held in buffer it % S.
-        // Rounds it+1 .. it+S-1 are in flight while round it is computed.
         const int ktiles = (g.K + BK - 1) / BK;
         const int rounds = (ktiles + KS - 1) / KS;
         auto exists = [&](int it) { return it < rounds && (KS == 1 || it * KS + group < ktiles); };
+        // Rounds it+1 .. it+S-1 are in flight while round it is computed.
 #pragma unroll
         for (int it = 0; it < S - 1; ++it)
             if (exists(it))
@@ -466,27 +494,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             if (exists(it + S - 1))
                 issue((it + S - 1) % S, ((it + S - 1) * KS + group) * BK);
             if (exists(it)) {
-                const float *pa = stage[it % S] + a_frag;
-                const float *pb = stage[it % S];
 #pragma unroll
                 for (int q = 0; q < BK / 8; ++q) {
-                    f32x4 a[FM];
-                    float b[4][FN];
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-                        a[i] = *reinterpret_cast<const f32x4 *>(pa + i * 32 * BK + 4 * ((2 * q + lh) ^ a_swz[i]));
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-                            b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
-#pragma unroll
-                    for (int s = 0; s < 4; ++s)
-#pragma unroll
-                        for (int i = 0; i < FM; ++i)
-#pragma unroll
-                            for (int j = 0; j < FN; ++j)
-                                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][s], b[s][j], acc[i][j], 0, 0, 0);
+                    Frag f;
+                    read_frag(f, it % S, q);
+                    mma(f);
                 }
             }
         }
