@@ -9,9 +9,10 @@ operands already resident in HBM.  The default workload is M = N = K = 8192.
 Timing follows the pages' method: W untimed warm-ups, then K timed calls with
 a device synchronisation on both sides; HIP events around each call on the
 stream it is enqueued on give the per-launch kernel time used for the
-roofline.  ``--table`` also times the 2048^3 case and every other workload
-shape (on stderr; their warm-up also runs for at least 0.2 s, since those
-kernels are short).  The last stdout line is one JSON object.
+roofline.  Every run also times 2048^3, the metric's second size, and
+reports it inside ``config``; ``--table`` adds every other workload shape (on
+stderr).  Short kernels get at least 0.2 s of warm-up so they are not timed
+while the clock ramps up.  The last stdout line is one JSON object.
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ METRIC = "FP32 GEMM TFLOPS and % of FP32 peak at M=N=K=2048 and 8192"
 PEAK_FP32_MATRIX_TFLOPS = 157.3     # MI355X dense FP32 MFMA
 PEAK_HBM_GBS = 8000.0
 
+SECOND_SHAPE = (2048, 2048, 2048)
 TABLE = [(512, 512, 512), (1025, 1023, 1000), (1, 1, 1), (17, 33, 65), (1000, 1000, 1000),
          (2048, 2048, 2048), (8192, 8192, 8192), (8192, 8192, 128), (16384, 64, 4096),
          (64, 16384, 4096), (4096, 4096, 16384)]
@@ -175,10 +177,19 @@ def main():
     M, N, K = args.shape
     head = time_gemm(torch, gb, M, N, K, args.steps, args.warmup, args.config)
     log(json.dumps(head))
+    peak = gb.gemm_f32_device_peak(0)
+    log(f"derived FP32 matrix peak: {peak['compute_units']} CUs x 256 FLOP/clk x "
+        f"{peak['clock_khz'] / 1e3:.0f} MHz = {peak['tflops']:.1f} TFLOP/s")
+    # The metric is quoted at 2048^3 as well: time it on every run (about a
+    # second) and report it beside the headline workload.
+    second = None
+    if (M, N, K) != SECOND_SHAPE:
+        second = time_gemm(torch, gb, *SECOND_SHAPE, args.steps, args.warmup, args.config, min_warm_s=0.2)
+        log(json.dumps(second))
     extra = {}
     if args.table:
         for shp in TABLE:
-            if tuple(shp) == (M, N, K):
+            if tuple(shp) in ((M, N, K), SECOND_SHAPE):
                 continue
             r = time_gemm(torch, gb, *shp, args.steps, args.warmup, args.config, min_warm_s=0.2)
             extra["x".join(map(str, shp))] = round(r["tflops_event_mean"], 3)
@@ -207,6 +218,15 @@ def main():
                      "frac": round(achieved / PEAK_FP32_MATRIX_TFLOPS, 4),
                      "traffic": measured_traffic(head["kernel"], M, N, K)},
     }
+    line["config"]["derived_peak"] = {"compute_units": peak["compute_units"],
+                                      "clock_mhz": round(peak["clock_khz"] / 1e3),
+                                      "tflops": round(peak["tflops"], 1)}
+    if second is not None:
+        tag = "x".join(map(str, SECOND_SHAPE))
+        line["config"][f"sgemm_{tag}"] = {
+            "kernel": second["kernel"], "event_us_mean": round(second["event_ms_mean"] * 1e3, 1),
+            "tflops": round(second["tflops_event_mean"], 3),
+            "pct_of_fp32_matrix_peak": round(100.0 * second["tflops_event_mean"] / PEAK_FP32_MATRIX_TFLOPS, 2)}
     if extra:
         line["config"]["other_tflops"] = extra
     if not args.no_cpu_baseline:

@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_f32_config_info.restype = i
         lib.gemm_f32_describe.argtypes = [i, i, i, i, p, i, p, i, p, i, ctypes.c_char_p, i]
         lib.gemm_f32_describe.restype = i
+        lib.gemm_f32_device_peak.argtypes = [i, ip, ip, ctypes.POINTER(ctypes.c_double)]
+        lib.gemm_f32_device_peak.restype = i
         lib.gemm_f32_status_string.argtypes = [i]
         lib.gemm_f32_status_string.restype = ctypes.c_char_p
         _lib = lib
@@ -91,6 +93,16 @@ def gemm_f32_config_info(config: int, occupancy: bool = False) -> dict:
     if occupancy:
         out["blocks_per_cu"] = vals[4].value
     return out
+
+
+def gemm_f32_device_peak(device: int = 0) -> dict:
+    """{'compute_units', 'clock_khz', 'tflops'}: the FP32 matrix-core peak derived
+    from the device's properties (needs a GPU)."""
+    cu, khz, tf = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_double(0.0)
+    rc = load().gemm_f32_device_peak(device, ctypes.byref(cu), ctypes.byref(khz), ctypes.byref(tf))
+    if rc != GEMM_F32_OK:
+        raise GemmError(rc, "gemm_f32_device_peak")
+    return dict(compute_units=cu.value, clock_khz=khz.value, tflops=tf.value)
 
 
 def gemm_f32_describe(config, M, N, K, A, lda, B, ldb, C, ldc) -> tuple[int, str]:

@@ -77,6 +77,15 @@ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int group,
     tn = r / rows;
 }
 
+// Epilogue store of one C element.  C is written once and not read again by
+// the kernel, so the store is marked non-temporal: it streams to memory
+// instead of displacing the A and B panels other workgroups still read from
+// L2 (measured +1 % on the store-heavy 8192 x 8192 x 128 and on 2048^3).
+__device__ inline void store_c(float *p, float v)
+{
+    __builtin_nontemporal_store(v, p);
+}
+
 // ---------------------------------------------------------------------------
 // Guarded loads: 4 consecutive elements of one row, +0.0 outside the matrix.
 // VEC = true needs a 16-byte aligned address and a row length that is a
@@ -271,7 +280,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
                 for (int r = 0; r < 16; ++r) {
                     const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
                     if (row < g.M && col < g.N)
-                        g.C[(int64_t)row * g.ldc + col] = acc[i][j][r];
+                        store_c(&g.C[(int64_t)row * g.ldc + col], acc[i][j][r]);
                 }
             }
         }
@@ -549,7 +558,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     for (int r = 0; r < 16; ++r) {
                         const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
                         if (row < g.M && col < g.N)
-                            g.C[(int64_t)row * g.ldc + col] = acc[i][j][r];
+                            store_c(&g.C[(int64_t)row * g.ldc + col], acc[i][j][r]);
                     }
                 }
             }
@@ -936,6 +945,24 @@ int gemm_f32_config_info(int config, int *bm, int *bn, int *bk, int *threads, in
             return GEMM_F32_ERR_LAUNCH;
         *blocks_per_cu = n;
     }
+    return GEMM_F32_OK;
+}
+
+int gemm_f32_device_peak(int device, int *compute_units, int *clock_khz, double *tflops)
+{
+    // One v_mfma_f32_32x32x2_f32 is 32 * 32 * 2 multiply-adds (4096 FLOP)
+    // and occupies a SIMD's matrix core for 64 cycles; a compute unit has 4
+    // SIMDs, so 256 FLOP per clock.
+    constexpr double kFlopPerClockPerCU = 4 * 4096.0 / 64;
+    int cu = 0, khz = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess ||
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeClockRate, device) != hipSuccess) {
+        (void)hipGetLastError();
+        return GEMM_F32_ERR_LAUNCH;
+    }
+    if (compute_units) *compute_units = cu;
+    if (clock_khz) *clock_khz = khz;
+    if (tflops) *tflops = cu * kFlopPerClockPerCU * (khz * 1e3) / 1e12;
     return GEMM_F32_OK;
 }
 

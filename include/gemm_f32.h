@@ -121,6 +121,16 @@ GEMM_F32_API int gemm_f32_describe(int config, int M, int N, int K,
                                    const float *C, int ldc,
                                    char *buf, int buflen);
 
+/*
+ * The FP32 matrix-core peak of HIP device `device` derived from its
+ * properties: compute units x 256 FLOP per clock (four SIMDs, each finishing
+ * one 32x32x2 FP32 MFMA, 4096 FLOP, every 64 cycles) x the peak engine clock
+ * the runtime reports.  Any output pointer may be NULL.  Without a usable
+ * device the call returns GEMM_F32_ERR_LAUNCH and writes nothing.
+ */
+GEMM_F32_API int gemm_f32_device_peak(int device, int *compute_units, int *clock_khz,
+                                      double *tflops);
+
 /* Static text for a return code. */
 GEMM_F32_API const char *gemm_f32_status_string(int status);
 

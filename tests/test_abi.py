@@ -152,3 +152,11 @@ def test_config_info_matches_names():
         assert info["threads"] % 64 == 0 and 64 <= info["threads"] <= 1024
     with pytest.raises(gb.GemmError):
         gb.gemm_f32_config_info(gb.gemm_f32_num_configs())
+
+
+def test_device_peak_without_a_device_is_an_error():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(gb.GemmError):
+        gb.gemm_f32_device_peak(0)

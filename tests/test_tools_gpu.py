@@ -34,3 +34,10 @@ def test_report_row(cuda):
     r = report.row_for(cuda, 256, steps=2, warmup=1)
     assert r["check"] == "bit-exact" and r["tflops"] > 0 and r["blocks_per_cu"] >= 1
     assert abs(r["ai"] - 2.0 * 256 ** 3 / (12.0 * 256 * 256)) < 1e-9
+
+
+def test_device_peak(cuda):
+    p = gb.gemm_f32_device_peak(0)
+    assert p["compute_units"] == cuda.cuda.get_device_properties(0).multi_processor_count
+    assert 1_000_000 <= p["clock_khz"] <= 4_000_000
+    assert p["tflops"] == pytest.approx(p["compute_units"] * 256 * p["clock_khz"] * 1e3 / 1e12)
