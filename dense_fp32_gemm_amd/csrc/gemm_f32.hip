@@ -77,6 +77,19 @@ __device__ inline void tile_coords(int t, int tiles_m, int tiles_n, int group,
     tn = r / rows;
 }
 
+// Stream-K work split: the iters = tiles x K-panels units of work, taken in
+// tile order, are cut into `workers` contiguous ranges of nearly equal length;
+// range b is [floor(b*iters/workers), floor((b+1)*iters/workers)), computed
+// without forming the 128-bit product.  When there are at least as many tiles
+// as workers every range is at least one tile's panels long, so a tile meets
+// at most two ranges.
+__device__ inline void streamk_range(int b, int workers, int64_t iters, int64_t &lo, int64_t &hi)
+{
+    const int64_t q = iters / workers, r = iters % workers;
+    lo = q * b + r * b / workers;
+    hi = q * (b + 1) + r * (b + 1) / workers;
+}
+
 // Epilogue store of one C element.  C is written once and not read again by
 // the kernel, so the store is marked non-temporal: it streams to memory
 // instead of displacing the A and B panels other workgroups still read from
@@ -333,13 +346,14 @@ __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_bas
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, offset, 0, 0, 0);
 }
 
-template <class T, bool VEC_A, bool VEC_B>
+template <class T, bool VEC_A, bool VEC_B, bool SK = false>
 __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
     constexpr int NW = T::kGroupWaves;                // waves per K-split group
     constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
+    static_assert(!SK || KS == 1, "stream-K splits K across workgroups, not inside one");
     static_assert(BK == 16 || BK == 32, "the A layout permutes the 16-byte chunks of 16- or 32-deep rows");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
     constexpr int kA = BM * BK;                       // floats per A panel
@@ -415,8 +429,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     float (*stage)[kStage] = lds[group];   // this group's ring of S buffers
 
     const int total = g.tiles_m * g.tiles_n;
-    for (int w = blockIdx.x; w < total; w += gridDim.x) {
-        const int t = (int)gridDim.x == total ? xcd_contiguous(w, total) : w;
+    const int ktiles = (g.K + BK - 1) / BK;
+
+    // Output tile t over K-panels [p_begin, p_end).  A tile whose panels are
+    // split between two workgroups (stream-K) adds its partial sum to C,
+    // which holds +0.0 there beforehand; every other tile stores.
+    auto work = [&](int t, int p_begin, int p_end) {
         int tm, tn;
         tile_coords(t, g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
         const int m0 = tm * BM;
@@ -480,16 +498,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[s][j], acc[i][j], 0, 0, 0);
         };
 
-        // Group `group` takes panels group, group + KS, group + 2*KS, ...;
-        // round `it` is its panel it*KS + group, held in buffer it % S.
-        const int ktiles = (g.K + BK - 1) / BK;
-        const int rounds = (ktiles + KS - 1) / KS;
-        auto exists = [&](int it) { return it < rounds && (KS == 1 || it * KS + group < ktiles); };
+        // Group `group` takes panels p_begin + group, + KS, + 2*KS, ...;
+        // round `it` is its panel p_begin + it*KS + group, held in buffer
+        // it % S.
+        const int npanels = p_end - p_begin;
+        const int rounds = (npanels + KS - 1) / KS;
+        auto exists = [&](int it) { return it < rounds && (KS == 1 || it * KS + group < npanels); };
+        auto panel_k = [&](int it) { return (p_begin + it * KS + group) * BK; };
         // Rounds it+1 .. it+S-1 are in flight while round it is computed.
 #pragma unroll
         for (int it = 0; it < S - 1; ++it)
             if (exists(it))
-                issue(it, (it * KS + group) * BK);
+                issue(it, panel_k(it));
         for (int it = 0; it < rounds; ++it) {
             // Round it has landed once no more than the loads of the rounds
             // after it (up to S-2 of them, kLoads each) are outstanding; the
@@ -501,7 +521,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
             if (exists(it + S - 1))
-                issue((it + S - 1) % S, ((it + S - 1) * KS + group) * BK);
+                issue((it + S - 1) % S, panel_k(it + S - 1));
             if (exists(it)) {
 #pragma unroll
                 for (int q = 0; q < BK / 8; ++q) {
@@ -548,6 +568,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             }
         }
 
+        const bool shared = SK && (p_begin != 0 || p_end != ktiles);
         if (group == 0) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
@@ -557,14 +578,57 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                        if (row < g.M && col < g.N)
-                            store_c(&g.C[(int64_t)row * g.ldc + col], acc[i][j][r]);
+                        if (row < g.M && col < g.N) {
+                            float *c = &g.C[(int64_t)row * g.ldc + col];
+                            if (shared)
+                                unsafeAtomicAdd(c, acc[i][j][r]);
+                            else
+                                store_c(c, acc[i][j][r]);
+                        }
                     }
                 }
             }
         }
+    };
+
+    if (SK) {
+        int64_t lo, hi;
+        streamk_range(xcd_contiguous(blockIdx.x, gridDim.x), gridDim.x, (int64_t)total * ktiles, lo, hi);
+        while (lo < hi) {
+            const int t = (int)(lo / ktiles);
+            const int p0 = (int)(lo - (int64_t)t * ktiles);
+            const int p1 = hi - lo < ktiles - p0 ? p0 + (int)(hi - lo) : ktiles;
+            work(t, p0, p1);
+            lo += p1 - p0;
+        }
+    } else {
+        for (int w = blockIdx.x; w < total; w += gridDim.x)
+            work((int)gridDim.x == total ? xcd_contiguous(w, total) : w, 0, ktiles);
     }
 }
+
+// Stream-K leaves each tile shared by two workgroups to be summed in C: both
+// add their partial sums atomically, so C must hold +0.0 there first.  Block
+// b looks at the start of workgroup range b + 1; if it falls strictly inside
+// a tile, that tile is shared and this block clears it (clipped to M x N).
+// As no two range starts fall inside one tile, each tile is cleared once.
+template <class T>
+__global__ __launch_bounds__(256) void zero_shared_tiles(GemmArgs g, int workers)
+{
+    const int ktiles = (g.K + T::BK - 1) / T::BK;
+    int64_t start, end;
+    streamk_range(blockIdx.x + 1, workers, (int64_t)g.tiles_m * g.tiles_n * ktiles, start, end);
+    if (start % ktiles == 0)
+        return;
+    int tm, tn;
+    tile_coords((int)(start / ktiles), g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
+    const int rows = min(T::BM, g.M - tm * T::BM), cols = min(T::BN, g.N - tn * T::BN);
+    float *c = g.C + (int64_t)tm * T::BM * g.ldc + (int64_t)tn * T::BN;
+    for (int e = threadIdx.x; e < rows * T::BN; e += blockDim.x)
+        if (e % T::BN < cols)
+            c[(int64_t)(e / T::BN) * g.ldc + e % T::BN] = 0.f;
+}
+
 
 // ---------------------------------------------------------------------------
 // Vector-FMA kernel: 64 x 64 tile, 256 threads, 4 x 4 outputs per thread.
@@ -685,6 +749,9 @@ enum ConfigId {
     kCfgDma64x128K32,
     kCfgDma128x64K32,
     kCfgDma128x128K32,
+    kCfgDma64x64K32SK,
+    kCfgDma128x128K32W16SK,
+    kCfgDma256x256W16SK,
     kNumConfigs
 };
 
@@ -721,6 +788,24 @@ template <class T, bool VA, bool VB>
 struct DmaKernel {
     static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB>;
 };
+template <class T, bool VA, bool VB>
+struct DmaStreamKKernel {
+    static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB, true>;
+};
+
+// Stream-K: clear the tiles two workgroups will share, then run the
+// workers (one per compute unit) on the same stream.
+template <class T>
+hipError_t launch_streamk(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
+{
+    if (grid > 1) {
+        zero_shared_tiles<T><<<grid - 1, 256, 0, s>>>(g, grid);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return Launch<T, DmaStreamKKernel>::run(g, va, vb, grid, s);
+}
 
 hipError_t launch_valu(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
 {
@@ -742,18 +827,26 @@ struct ConfigInfo {
     bool dma;                    // direct-to-LDS (32-bit panel offsets)
     hipError_t (*launch)(const GemmArgs &, bool, bool, int, hipStream_t);
     int (*occupancy)();
+    bool streamk;                // one worker per CU over all tiles' K-panels
 };
 
 template <class T, template <class, bool, bool> class Kernel>
 constexpr ConfigInfo config(const char *name, bool dma)
 {
     return {name, T::BM, T::BN, T::BK, T::kThreads, dma, &Launch<T, Kernel>::run,
-            &Launch<T, Kernel>::occupancy};
+            &Launch<T, Kernel>::occupancy, false};
+}
+
+template <class T>
+constexpr ConfigInfo config_streamk(const char *name)
+{
+    return {name, T::BM, T::BN, T::BK, T::kThreads, true, &launch_streamk<T>,
+            &Launch<T, DmaStreamKKernel>::occupancy, true};
 }
 
 // Indexed by ConfigId.
 const ConfigInfo kConfigs[kNumConfigs] = {
-    {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu},
+    {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu, false},
     config<Tile256x256W16, DmaKernel>("dma_256x256x16_w16", true),
     config<Tile128x128W16, DmaKernel>("dma_128x128x16_w16", true),
     config<Tile128x128, DmaKernel>("dma_128x128x16", true),
@@ -772,6 +865,9 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config<Tile64x128K32, DmaKernel>("dma_64x128x32", true),
     config<Tile128x64K32, DmaKernel>("dma_128x64x32", true),
     config<Tile128x128K32, DmaKernel>("dma_128x128x32", true),
+    config_streamk<Tile64x64K32>("dma_64x64x32_sk"),
+    config_streamk<Tile128x128K32W16>("dma_128x128x32_w16_sk"),
+    config_streamk<Tile256x256W16>("dma_256x256x16_w16_sk"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -799,6 +895,12 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    64 x 64 with K split over four wave groups inside the workgroup;
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
+// When a tile count just above a multiple of 256 would leave most CUs idle
+// in the last round, the stream-K twin of the 256 x 256 or 64 x 64 choice
+// spreads all tiles' K-panels evenly over one workgroup per CU (measured:
+// 5000^3 1921 us against 2381, (1025, 1023, 1000) 42 us against 46); for the
+// 128 x 128 choice only with K >= 2048 (2560^3: 282 us against 315), since
+// below that 64 x 64 tiles do better ((2176, 2100, 1000): 93 us against 108).
 // Below the two largest tiles every choice uses 32-deep K-panels: those
 // tiles give each wave few MFMAs per panel, so halving the number of panels
 // halves the per-panel barrier, wait and LDS-latency cost.  Problems with
@@ -814,17 +916,30 @@ int select_config(int M, int N, int K, bool dma_ok)
             return kCfgStaged128x128;
         return kCfgStaged64x64;
     }
+    // The busiest CU has ceil(tiles / CUs) tiles.  The last round of tiles
+    // leaves more than a fifth of the CU-rounds idle when this is true:
+    auto unbalanced = [&](int c) {
+        const int64_t t = tiles(c);
+        return 5 * t < 4 * ceil_div(t, kComputeUnits) * kComputeUnits;
+    };
     if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128;
     if (tiles(kCfgDma256x256W16) >= kComputeUnits)
-        return kCfgDma256x256W16;
-    if (tiles(kCfgDma128x128K32W16) >= kComputeUnits)
-        return kCfgDma128x128K32W16;
+        return unbalanced(kCfgDma256x256W16) ? kCfgDma256x256W16SK : kCfgDma256x256W16;
+    if (tiles(kCfgDma128x128K32W16) >= kComputeUnits) {
+        if (!unbalanced(kCfgDma128x128K32W16))
+            return kCfgDma128x128K32W16;
+        // Stream-K's extra launch and split-tile passes pay off over a long
+        // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
+        return K >= 2048 ? kCfgDma128x128K32W16SK : kCfgDma64x64K32;
+    }
     if (tiles(kCfgDma64x64K32) < 2 * kComputeUnits && K >= 2048)
         return kCfgDma64x64K32S4;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * kComputeUnits)
         return wide;
+    if (tiles(kCfgDma64x64K32) > kComputeUnits && unbalanced(kCfgDma64x64K32))
+        return kCfgDma64x64K32SK;
     return kCfgDma64x64K32;
 }
 
@@ -879,7 +994,10 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     plan->config = c;
     plan->tiles_m = (int)tm;
     plan->tiles_n = (int)tn;
-    plan->grid = (int)(tm * tn < kMaxGrid ? tm * tn : kMaxGrid);
+    if (kConfigs[c].streamk)
+        plan->grid = (int)(tm * tn < kComputeUnits ? tm * tn : kComputeUnits);
+    else
+        plan->grid = (int)(tm * tn < kMaxGrid ? tm * tn : kMaxGrid);
     plan->vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
     plan->vec_b = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
     return GEMM_F32_OK;

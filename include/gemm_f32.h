@@ -26,8 +26,14 @@
  * Memory and ownership: A, B and C are DEVICE pointers owned by the caller,
  * 4-byte aligned (16-byte alignment of the base and of lda/ldb/ldc*4 lets the
  * kernels use 128-bit loads, but is not required).  C must not overlap A or
- * B.  The library allocates no device memory and keeps no state between
- * calls; it is safe to call from several host threads.
+ * B, and must be ordinary device memory (hipMalloc): on shapes whose tile
+ * count would leave most compute units idle in the last round, the library
+ * splits the K range of some output tiles between two workgroups, first
+ * clears those tiles and then adds both partial sums into C with hardware
+ * atomic float adds.  Exactly two addends on +0.0 commute, so the result is
+ * the same whichever lands first: every configuration is deterministic.  The
+ * library allocates no device memory and keeps no state between calls; it is
+ * safe to call from several host threads.
  *
  * Asynchrony: every call only enqueues work on `stream` (a hipStream_t; 0 is
  * the null stream) and returns.  Errors detected while the kernels run are

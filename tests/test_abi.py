@@ -134,6 +134,11 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
     ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
     ((1000, 1000, 1000), "dma_64x64x32 "), ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
+    # 272, 400 and 400 tiles: the last round would leave most CUs idle
+    ((1025, 1023, 1000), "dma_64x64x32_sk "), ((2560, 2560, 2560), "dma_128x128x32_w16_sk "),
+    ((5000, 5000, 5000), "dma_256x256x16_w16_sk "),
+    # 289 128 x 128 tiles but K < 2048: 1122 64 x 64 tiles instead
+    ((2176, 2100, 1000), "dma_64x64x32 "),
 ])
 def test_selection(shape, name):
     M, N, K = shape
@@ -160,3 +165,12 @@ def test_device_peak_without_a_device_is_an_error():
         pytest.skip("a GPU is present")
     with pytest.raises(gb.GemmError):
         gb.gemm_f32_device_peak(0)
+
+
+def test_streamk_grid_is_one_worker_per_compute_unit():
+    cfg = gb.config_names().index("dma_64x64x32_sk")
+    rc, text = gb.gemm_f32_describe(cfg, 1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
+    assert rc == gb.GEMM_F32_OK and "tiles=17x16 grid=256 " in text, text
+    # fewer tiles than compute units: one worker per tile, nothing shared
+    rc, text = gb.gemm_f32_describe(cfg, 300, 300, 1000, FAKE, 1000, FAKE, 300, FAKE, 300)
+    assert rc == gb.GEMM_F32_OK and "tiles=5x5 grid=25 " in text, text

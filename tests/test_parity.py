@@ -320,3 +320,39 @@ def test_random_shapes_layouts_and_configs(dev):
         A, B = inputs.quarter_step(M, N, K, 11 + trial, 13 + trial)
         got, _ = gpu_gemm(A, B, config, dev, pad=pad, offset=off)
         assert_bit_exact(got, oracle.gemm(A, B), f"trial {trial}: {(M, N, K)} config {config} pad {pad} off {off}")
+
+
+# ---------------------------------------------------------------------------
+# Stream-K: more tiles than compute units, so the K-panels of some tiles are
+# split between two workgroups that add their partial sums into C.
+# ---------------------------------------------------------------------------
+STREAMK = [("dma_64x64x32_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
+           ("dma_128x128x32_w16_sk", (2176, 2100, 1000)),
+           ("dma_256x256x16_w16_sk", (4352, 4200, 200))]
+
+
+@pytest.mark.parametrize("name,shape", STREAMK, ids=[f"{n}-{'x'.join(map(str, s))}" for n, s in STREAMK])
+def test_streamk_bit_exact_and_padding_kept(dev, name, shape):
+    M, N, K = shape
+    cfg = gb.config_names().index(name)
+    rc, desc = gb.gemm_f32_describe(cfg, M, N, K, 16, K, 16, N, 16, N + 5)
+    assert rc == gb.GEMM_F32_OK and "grid=256 " in desc, desc
+    A, B = operands("quarter", M, N, K)
+    got, full = gpu_gemm(A, B, cfg, dev, pad=(0, 0, 5))
+    assert_bit_exact(got, oracle.gemm(A, B), f"{shape} {name}")
+    body = full[:M * (N + 5)].reshape(M, N + 5)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 5):]).all()
+
+
+@pytest.mark.parametrize("name,shape", STREAMK[:3], ids=[f"{n}-{'x'.join(map(str, s))}" for n, s in STREAMK[:3]])
+def test_streamk_uniform_within_tolerance_and_deterministic(dev, name, shape):
+    """Each shared tile receives exactly two partial sums added to +0.0, and
+    binary32 addition is commutative, so the result does not depend on which
+    workgroup finishes first: repeated calls agree bit for bit."""
+    cfg = gb.config_names().index(name)
+    A, B = operands("uniform", *shape)
+    first, _ = gpu_gemm(A, B, cfg, dev)
+    assert_close(first, oracle.gemm(A, B), f"{shape} {name}")
+    for _ in range(3):
+        again, _ = gpu_gemm(A, B, cfg, dev)
+        assert_bit_exact(again, first, f"{shape} {name} repeat")
