@@ -450,8 +450,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 const bool ok = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K;
                 buffer_to_lds(ra, &stage[buf][(gw * kLoadsA + j) * kSpanA], ok ? a_off[j] : kOutOfRange, 4 * kVecA);
             }
+            // The B range ends after B's last element (K-1, N-1): a 4-float
+            // chunk that starts in the last row before column N but runs past
+            // it reads zeros there instead of memory beyond B.
+            const int64_t b_left = 4 * ((int64_t)(g.K - 1 - k0) * g.ldb + (g.N - n0));
             const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0, (int)kOutOfRange, kRawBufferFlags);
+                (void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0,
+                (int)(b_left < (int64_t)kOutOfRange ? b_left : (int64_t)kOutOfRange), kRawBufferFlags);
 #pragma unroll
             for (int j = 0; j < kLoadsB; ++j) {
                 if (!kEvenB && gw * kLoadsB + j >= kInstB)
@@ -998,8 +1003,19 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
         plan->grid = (int)(tm * tn < kComputeUnits ? tm * tn : kComputeUnits);
     else
         plan->grid = (int)(tm * tn < kMaxGrid ? tm * tn : kMaxGrid);
-    plan->vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
-    plan->vec_b = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+    if (kConfigs[c].dma) {
+        // Direct-to-LDS loads move 16 bytes from any 4-byte aligned address
+        // (checked on gfx950 together with the per-dword range check).  A
+        // 4-float chunk of an A row never crosses column K when K % 4 == 0.  A
+        // chunk of B that crosses column N only feeds C columns >= N, which
+        // are never stored, and the panel's buffer range ends at B's last
+        // element, so nothing beyond B is read.
+        plan->vec_a = K % 4 == 0;
+        plan->vec_b = true;
+    } else {
+        plan->vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
+        plan->vec_b = aligned16(B) && ldb % 4 == 0 && N % 4 == 0;
+    }
     return GEMM_F32_OK;
 }
 

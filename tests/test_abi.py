@@ -103,13 +103,20 @@ def test_describe():
     assert rc == gb.GEMM_F32_ERR_DIM and text.startswith("invalid")
     rc, text = gb.gemm_f32_describe(-1, 8192, 8192, 8192, FAKE, 8192, FAKE, 8192, FAKE, 8192)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma") and "load_a=x4 load_b=x4" in text
+    # direct-to-LDS loads: 128-bit from any 4-byte aligned address; A only
+    # when K % 4 == 0 (its chunks must not cross column K), B always
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
-    assert rc == gb.GEMM_F32_OK and "load_a=x4 load_b=x1" in text
+    assert rc == gb.GEMM_F32_OK and "load_a=x4 load_b=x4" in text
+    rc, text = gb.gemm_f32_describe(-1, 512, 512, 512, FAKE + 4, 515, FAKE + 8, 517, FAKE, 512)
+    assert text.startswith("dma") and "load_a=x4 load_b=x4" in text, text
+    rc, text = gb.gemm_f32_describe(-1, 512, 512, 1001, FAKE, 1001, FAKE, 512, FAKE, 512)
+    assert text.startswith("dma") and "load_a=x1 load_b=x4" in text, text
     rc, text = gb.gemm_f32_describe(-1, 1, 1, 1, FAKE, 1, FAKE, 1, FAKE, 1)
     assert rc == gb.GEMM_F32_OK and text.startswith("valu")
-    # 16-byte alignment of the base decides the load width as well
-    rc, text = gb.gemm_f32_describe(-1, 512, 512, 512, FAKE + 4, 512, FAKE, 512, FAKE, 512)
-    assert "load_a=x1 load_b=x4" in text
+    # the register-staged kernel keeps 16-byte alignment for its 128-bit loads
+    staged = gb.config_names().index("staged_64x64x16")
+    rc, text = gb.gemm_f32_describe(staged, 512, 512, 512, FAKE + 4, 512, FAKE, 512, FAKE, 512)
+    assert "load_a=x1 load_b=x4" in text, text
 
 
 def test_wide_rows_fall_back_to_staged_kernels():

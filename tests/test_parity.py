@@ -356,3 +356,20 @@ def test_streamk_uniform_within_tolerance_and_deterministic(dev, name, shape):
     for _ in range(3):
         again, _ = gpu_gemm(A, B, cfg, dev)
         assert_bit_exact(again, first, f"{shape} {name} repeat")
+
+
+@pytest.mark.parametrize("config", [c for c in CONFIGS if gb.gemm_f32_config_name(c).startswith("dma")],
+                         ids=[n for n in CONFIG_IDS if n.startswith("dma")])
+def test_b_chunks_crossing_column_n_leave_c_clean(dev, config):
+    """N % 4 != 0 with NaN in B's row padding: 128-bit B loads that run past
+    column N pick up NaN (or the next row) in LDS columns >= N, which must
+    not reach any stored element; K % 4 == 0 with NaN in A's padding, and
+    unaligned bases, exercise 128-bit A loads from 4-byte aligned rows."""
+    M, N, K = 130, 270, 72
+    A, B = operands("quarter", M, N, K)
+    for pad, off in (((0, 0, 0), (0, 0, 0)), ((1, 3, 2), (0, 0, 0)), ((3, 1, 0), (1, 2, 3))):
+        got, full = gpu_gemm(A, B, config, dev, pad=pad, offset=off)
+        assert_bit_exact(got, oracle.gemm(A, B), f"pad {pad} off {off}")
+        ldc = N + pad[2]
+        body = full[off[2]:off[2] + M * ldc].reshape(M, ldc)
+        assert np.isnan(body[:, N:]).all() and np.isnan(full[off[2] + M * ldc:]).all()
