@@ -312,7 +312,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 // outside the resource's range reads as zero, so ragged rows, columns and
 // K-tails are zero-filled by pointing their lanes at an out-of-range offset.
 //
-// LDS layouts (per panel, BK = 16 or 32):
+// LDS layouts (per panel, BK = 16, 32 or 64):
 //  * A: [BM][BK] floats, the BK/4 16-byte chunks of row r permuted by
 //    chunk ^ swz_a<BK>(r), so that the 128-bit fragment reads (32 rows, one
 //    chunk per lane half) run without bank conflicts.
@@ -329,12 +329,13 @@ constexpr int kRawBufferFlags = 0x00020000;      // dword 3 of a raw buffer reso
 // Chosen by measurement (SQ_LDS_BANK_CONFLICT on 128-bit fragment reads of
 // 32 consecutive rows): for 64-byte rows, rows four apart share banks and
 // (r >> 2) & 3 rotates them onto different chunks, which reads with no
-// conflict cycles; for 128-byte rows (r ^ (r >> 3)) & 7 does.
+// conflict cycles; for 128-byte rows (r ^ (r >> 3)) & 7 does, and for
+// 256-byte rows r & 15.
 template <int BK>
 __device__ inline int swz_a(int r)
 {
-    static_assert(BK == 16 || BK == 32, "A-panel swizzles exist for 16- and 32-deep panels");
-    return BK == 16 ? (r >> 2) & 3 : (r ^ (r >> 3)) & 7;
+    static_assert(BK == 16 || BK == 32 || BK == 64, "A-panel swizzles exist for 16-, 32- and 64-deep panels");
+    return BK == 16 ? (r >> 2) & 3 : BK == 32 ? (r ^ (r >> 3)) & 7 : r & 15;
 }
 
 __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_base, uint32_t offset, int bytes)
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
     static_assert(!SK || KS == 1, "stream-K splits K across workgroups, not inside one");
-    static_assert(BK == 16 || BK == 32, "the A layout permutes the 16-byte chunks of 16- or 32-deep rows");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "the A layout permutes the 16-byte chunks of 16-, 32- or 64-deep rows");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
     constexpr int kA = BM * BK;                       // floats per A panel
     constexpr int kB = BK * BN;                       // floats per B panel
@@ -733,6 +734,7 @@ using Tile64x64K32S4 = MfmaTile<64, 64, 32, 2, 2, 4>;
 using Tile64x128K32 = MfmaTile<64, 128, 32, 2, 2>;
 using Tile128x64K32 = MfmaTile<128, 64, 32, 2, 2>;
 using Tile128x128K32 = MfmaTile<128, 128, 32, 2, 2>;
+using Tile64x64K64 = MfmaTile<64, 64, 64, 2, 2>;         // 64-deep panels
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -757,6 +759,8 @@ enum ConfigId {
     kCfgDma64x64K32SK,
     kCfgDma128x128K32W16SK,
     kCfgDma256x256W16SK,
+    kCfgDma64x64K64,
+    kCfgDma64x64K64SK,
     kNumConfigs
 };
 
@@ -873,6 +877,8 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_streamk<Tile64x64K32>("dma_64x64x32_sk"),
     config_streamk<Tile128x128K32W16>("dma_128x128x32_w16_sk"),
     config_streamk<Tile256x256W16>("dma_256x256x16_w16_sk"),
+    config<Tile64x64K64, DmaKernel>("dma_64x64x64", true),
+    config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -896,19 +902,20 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    (short K: per-tile start-up and the C store weigh more than reuse);
 //  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64;
 //  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
-//  * fewer than two 64 x 64 tiles per CU with K >= 2048 (skinny shapes):
+//  * at most one 64 x 64 tile per CU with K >= 2048 (skinny shapes):
 //    64 x 64 with K split over four wave groups inside the workgroup;
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // When a tile count just above a multiple of 256 would leave most CUs idle
-// in the last round, the stream-K twin of the 256 x 256 or 64 x 64 choice
-// spreads all tiles' K-panels evenly over one workgroup per CU (measured:
-// 5000^3 1921 us against 2381, (1025, 1023, 1000) 42 us against 46); for the
-// 128 x 128 choice only with K >= 2048 (2560^3: 282 us against 315), since
-// below that 64 x 64 tiles do better ((2176, 2100, 1000): 93 us against 108).
-// Below the two largest tiles every choice uses 32-deep K-panels: those
-// tiles give each wave few MFMAs per panel, so halving the number of panels
-// halves the per-panel barrier, wait and LDS-latency cost.  Problems with
+// in the last round, a stream-K twin spreads all tiles' K-panels evenly over
+// one workgroup per CU (measured: 5000^3 1921 us against 2381 for 256 x 256
+// tiles; (1025, 1023, 1000) 36.8 us against 42.4 for 64 x 64); for 128 x 128
+// tiles only with K >= 2048 (2560^3: 282 us against 315), since below that
+// 64 x 64 tiles do better ((2176, 2100, 1000): 93 us against 108).
+// Below the two largest tiles the choices use 32- or 64-deep K-panels: those
+// tiles give each wave few MFMAs per panel, so fewer, deeper panels cut the
+// per-panel barrier, wait and LDS-latency cost (64-deep: +6 to +9 % at 512^3,
+// 1000^3, 1024^3 and 768 x 768 x 2048 with one 64 x 64 tile per CU).  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
 int select_config(int M, int N, int K, bool dma_ok)
@@ -938,14 +945,21 @@ int select_config(int M, int N, int K, bool dma_ok)
         // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
         return K >= 2048 ? kCfgDma128x128K32W16SK : kCfgDma64x64K32;
     }
-    if (tiles(kCfgDma64x64K32) < 2 * kComputeUnits && K >= 2048)
+    if (tiles(kCfgDma64x64K32) <= kComputeUnits && K >= 2048)
         return kCfgDma64x64K32S4;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * kComputeUnits)
         return wide;
-    if (tiles(kCfgDma64x64K32) > kComputeUnits && unbalanced(kCfgDma64x64K32))
-        return kCfgDma64x64K32SK;
-    return kCfgDma64x64K32;
+    // 64 x 64 tiles.  Up to two per CU, one 4-wave workgroup per SIMD set
+    // leaves each SIMD a single wave, and 64-deep panels halve the per-panel
+    // barrier stalls that then show; with more, several workgroups share a
+    // CU and the smaller 32-deep panels (more resident workgroups) win.
+    // Barely more than one tile per CU: stream-K, so the few extra tiles do
+    // not double the time.
+    const int64_t t64 = tiles(kCfgDma64x64K64);
+    if (t64 > kComputeUnits && 4 * t64 <= 5 * kComputeUnits)
+        return kCfgDma64x64K64SK;
+    return t64 < 2 * kComputeUnits ? kCfgDma64x64K64 : kCfgDma64x64K32;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

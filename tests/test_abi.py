@@ -140,12 +140,18 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((4096, 4096, 16384), "dma_256x256x16_w16 "), ((1024, 8192, 8192), "dma_128x128x32_w16 "),
     ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
     ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
-    ((1000, 1000, 1000), "dma_64x64x32 "), ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
+    ((1000, 1000, 1000), "dma_64x64x64 "), ((512, 512, 512), "dma_64x64x64 "),
+    ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # 272, 400 and 400 tiles: the last round would leave most CUs idle
-    ((1025, 1023, 1000), "dma_64x64x32_sk "), ((2560, 2560, 2560), "dma_128x128x32_w16_sk "),
+    ((1025, 1023, 1000), "dma_64x64x64_sk "), ((2560, 2560, 2560), "dma_128x128x32_w16_sk "),
     ((5000, 5000, 5000), "dma_256x256x16_w16_sk "),
+    # 400 64 x 64 tiles: two rounds, resident together; 576: 32-deep panels
+    ((1280, 1280, 1280), "dma_64x64x64 "), ((1536, 1536, 1536), "dma_64x64x32 "),
     # 289 128 x 128 tiles but K < 2048: 1122 64 x 64 tiles instead
     ((2176, 2100, 1000), "dma_64x64x32 "),
+    # long K: the in-workgroup K-split only while there is one tile per CU
+    ((1024, 1024, 8192), "dma_64x64x32_ksplit4"), ((1025, 1025, 4096), "dma_64x64x64_sk "),
+    ((1300, 1300, 4096), "dma_64x64x64 "),
 ])
 def test_selection(shape, name):
     M, N, K = shape
@@ -175,7 +181,7 @@ def test_device_peak_without_a_device_is_an_error():
 
 
 def test_streamk_grid_is_one_worker_per_compute_unit():
-    cfg = gb.config_names().index("dma_64x64x32_sk")
+    cfg = gb.config_names().index("dma_64x64x64_sk")
     rc, text = gb.gemm_f32_describe(cfg, 1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and "tiles=17x16 grid=256 " in text, text
     # fewer tiles than compute units: one worker per tile, nothing shared

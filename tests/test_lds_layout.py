@@ -12,7 +12,7 @@ conflict cycles for both), not from a bank model.
 import pytest
 
 def swz_a(r, BK=16):
-    return (r >> 2) & 3 if BK == 16 else (r ^ (r >> 3)) & 7
+    return (r >> 2) & 3 if BK == 16 else (r ^ (r >> 3)) & 7 if BK == 32 else r & 15
 
 
 def a_store(BM, BK=16):
@@ -29,7 +29,7 @@ def b_store(BN, BK=16):
     return {(k, c): (k, c ^ (((k >> 2) & 1) * 32)) for k in range(BK) for c in range(BN)}
 
 
-@pytest.mark.parametrize("BK", [16, 32])
+@pytest.mark.parametrize("BK", [16, 32, 64])
 @pytest.mark.parametrize("BM,WM", [(256, 2), (256, 4), (128, 2), (128, 4), (64, 2)])
 def test_a_fragments_read_the_paired_k(BM, WM, BK):
     store = a_store(BM, BK)
@@ -44,7 +44,7 @@ def test_a_fragments_read_the_paired_k(BM, WM, BK):
                         assert store[(row, slot)] == (row, 8 * q + 4 * lh + s)
 
 
-@pytest.mark.parametrize("BK", [16, 32])
+@pytest.mark.parametrize("BK", [16, 32, 64])
 @pytest.mark.parametrize("BN,WN", [(256, 4), (256, 2), (128, 2), (128, 4), (64, 2)])
 def test_b_fragments_read_the_paired_k(BN, WN, BK):
     store = b_store(BN, BK)
@@ -65,6 +65,7 @@ def test_layouts_are_permutations():
     for r in range(256):
         assert sorted(c ^ swz_a(r, 16) for c in range(4)) == [0, 1, 2, 3]
         assert sorted(c ^ swz_a(r, 32) for c in range(8)) == list(range(8))
+        assert sorted(c ^ swz_a(r, 64) for c in range(16)) == list(range(16))
     for BN in (64, 128, 256):
-        for k in range(32):
+        for k in range(64):
             assert sorted(c ^ (((k >> 2) & 1) * 32) for c in range(BN)) == list(range(BN))
