@@ -900,7 +900,9 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 // with 16 waves when there are enough of them (256 compute units):
 //  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 4 waves
 //    (short K: per-tile start-up and the C store weigh more than reuse);
-//  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64;
+//  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64,
+//    32-deep panels (+1.5 % over 16-deep at 4096^3 and 8192^3 on one box,
+//    equal on another);
 //  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
 //  * at most one 64 x 64 tile per CU with K >= 2048 (skinny shapes):
 //    64 x 64 with K split over four wave groups inside the workgroup;
@@ -936,8 +938,8 @@ int select_config(int M, int N, int K, bool dma_ok)
     };
     if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128;
-    if (tiles(kCfgDma256x256W16) >= kComputeUnits)
-        return unbalanced(kCfgDma256x256W16) ? kCfgDma256x256W16SK : kCfgDma256x256W16;
+    if (tiles(kCfgDma256x256K32W16) >= kComputeUnits)
+        return unbalanced(kCfgDma256x256K32W16) ? kCfgDma256x256W16SK : kCfgDma256x256K32W16;
     if (tiles(kCfgDma128x128K32W16) >= kComputeUnits) {
         if (!unbalanced(kCfgDma128x128K32W16))
             return kCfgDma128x128K32W16;
@@ -998,11 +1000,11 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     }
     int c = config;
     if (c < 0) {
-        // Every direct-to-LDS configuration the rule can pick fits if the
-        // tallest A panel (256 rows) and the deepest B panel (32 rows) do.
-        const bool dma_ok = dma_offsets_fit(kConfigs[kCfgDma256x256W16], lda, ldb) &&
-                            dma_offsets_fit(kConfigs[kCfgDma128x128K32W16], lda, ldb);
-        c = select_config(M, N, K, dma_ok);
+        // The rule's direct-to-LDS choice, unless its panels are too tall or
+        // deep for 32-bit offsets at these leading dimensions.
+        c = select_config(M, N, K, true);
+        if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
+            c = select_config(M, N, K, false);
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
