@@ -124,7 +124,7 @@ __device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncol
 // Matrix-core kernel
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KSPLIT_ = 1, int STAGES_ = 2,
-          int GROUP_ = 8>
+          int GROUP_ = 8, int LOADERS_ = 0>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -151,9 +151,13 @@ struct MfmaTile {
     static constexpr int kChunksB = BK * BN / 4 / kThreads;
     static constexpr int kGroup = GROUP_;            // tile rows per raster group
     static constexpr int kStages = STAGES_;          // LDS panel buffers per K-split group
+    // Waves of each group that issue the direct-to-LDS panel loads (the
+    // lowest-numbered ones; 0: all of them).
+    static constexpr int kLoaders = LOADERS_ ? LOADERS_ : WAVES_M * WAVES_N;
 
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
     static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
+    static_assert(kLoaders >= 1 && kLoaders <= WAVES_M * WAVES_N, "loader waves");
 };
 
 // One v_mfma_f32_32x32x2_f32 adds, for the 32 x 32 block it accumulates,
@@ -363,13 +367,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int kVecA = VEC_A ? 4 : 1, kVecB = VEC_B ? 4 : 1;
     constexpr int kSpanA = kWaveSize * kVecA;         // floats one instruction moves
     constexpr int kSpanB = kWaveSize * kVecB;
-    // Load instructions per panel, dealt to the group's waves in order; when
-    // a panel has fewer instructions than NW times the per-wave count, the
-    // last waves skip the missing ones.
+    // Load instructions per panel, dealt in order to the group's first NL
+    // waves; when a panel has fewer instructions than NL times the per-wave
+    // count, the last of them skip the missing ones.  With 16 waves, letting
+    // only the first 8 load measured fastest: those waves issue first after
+    // each barrier, so the loads start at once, while the other 8 go straight
+    // to their fragment reads and MFMAs instead of queueing behind the loads
+    // (+3.6 % at 2048^3, +1.4 % at 8192^3; 4 or 12 loaders, or the last 8 or
+    // every other wave as loaders, were slower).
+    constexpr int NL = T::kLoaders;
     constexpr int kInstA = kA / kSpanA, kInstB = kB / kSpanB;
-    constexpr int kLoadsA = (kInstA + NW - 1) / NW;   // instructions per wave per panel
-    constexpr int kLoadsB = (kInstB + NW - 1) / NW;
-    constexpr bool kEvenA = kInstA % NW == 0, kEvenB = kInstB % NW == 0;
+    constexpr int kLoadsA = (kInstA + NL - 1) / NL;   // instructions per loader wave per panel
+    constexpr int kLoadsB = (kInstB + NL - 1) / NL;
+    constexpr bool kEvenA = kInstA % NL == 0, kEvenB = kInstB % NL == 0;
     static_assert(kA % kSpanA == 0 && kB % kSpanB == 0, "panel split");
     constexpr int S = T::kStages;
     constexpr int kLoads = kLoadsA + kLoadsB;         // per wave per round
@@ -382,7 +392,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 
     const int tid = threadIdx.x;
     const int lane = tid % kWaveSize;
-    const int wave = tid / kWaveSize;
+    // The wave index is the same in every lane; saying so keeps everything
+    // derived from it (LDS destinations of the panel loads, K-split group,
+    // loader role) in scalar registers instead of per-lane loops.
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWaveSize);
     const int group = KS == 1 ? 0 : wave / NW;        // K-split group
     const int gw = KS == 1 ? wave : wave % NW;        // wave within its group
     const int wave_m = gw / T::WAVES_N;
@@ -390,12 +403,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     const int li = lane % 32;
     const int lh = lane / 32;
 
-    // Slot -> source element maps, fixed for the whole kernel.
+    // Slot -> source element maps, fixed for the whole kernel (loader waves).
+    const bool loader = gw < NL;
+    const int lw = loader ? gw : 0;
     uint32_t a_off[kLoadsA];     // byte offset from the panel's (m0, k0) corner
     int a_r[kLoadsA], a_k[kLoadsA];
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
-        const int f = (gw * kLoadsA + j) * kSpanA + lane * kVecA;   // LDS slot (float index)
+        const int f = (lw * kLoadsA + j) * kSpanA + lane * kVecA;   // LDS slot (float index)
         const int r = f / BK, e = f % BK;
         const int k = 4 * ((e / 4) ^ swz_a<BK>(r)) + e % 4;
         a_r[j] = r;
@@ -406,7 +421,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     int b_k[kLoadsB], b_c[kLoadsB];
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
-        const int f = (gw * kLoadsB + j) * kSpanB + lane * kVecB;
+        const int f = (lw * kLoadsB + j) * kSpanB + lane * kVecB;
         const int k = f / BN;
         const int c = (f % BN) ^ (((k >> 2) & 1) * 32);
         b_k[j] = k;
@@ -431,6 +446,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 
     const int total = g.tiles_m * g.tiles_n;
     const int ktiles = (g.K + BK - 1) / BK;
+    const int64_t b_end = (int64_t)(g.K - 1) * g.ldb + g.N;   // floats from B to one past its last element
 
     // Output tile t over K-panels [p_begin, p_end).  A tile whose panels are
     // split between two workgroups (stream-K) adds its partial sum to C,
@@ -441,29 +457,51 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         const int m0 = tm * BM;
         const int n0 = tn * BN;
 
-        auto issue = [&](int buf, int k0) {
-            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(g.A + ((int64_t)m0 * g.lda + k0)), 0, (int)kOutOfRange, kRawBufferFlags);
+        // The loads of one panel: prepare() works out the panel corners and
+        // per-lane offsets, fire() builds the buffer resources and issues the
+        // loads (loader waves only).
+        struct Panel {
+            const float *a, *b;          // panel corners
+            int b_range;                 // bytes of B from b on
+            uint32_t oa[kLoadsA], ob[kLoadsB];
+        };
+        auto prepare = [&](int k0) {
+            Panel p;
+            p.a = g.A + ((int64_t)m0 * g.lda + k0);
+#pragma unroll
+            for (int j = 0; j < kLoadsA; ++j)
+                p.oa[j] = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K ? a_off[j] : kOutOfRange;
+            // When N % 4 != 0 a 4-float chunk can start before column N and
+            // run past it; the B range then ends after B's last element
+            // (K-1, N-1), so in the last row such a chunk reads zeros instead
+            // of memory beyond B.
+            const int64_t b_corner = (int64_t)k0 * g.ldb + n0;
+            const int64_t b_left = 4 * (b_end - b_corner);
+            p.b_range = (g.N & 3) && b_left < (int64_t)kOutOfRange ? (int)b_left : (int)kOutOfRange;
+            p.b = g.B + b_corner;
+#pragma unroll
+            for (int j = 0; j < kLoadsB; ++j)
+                p.ob[j] = k0 + b_k[j] < g.K && n0 + b_c[j] < g.N ? b_off[j] : kOutOfRange;
+            return p;
+        };
+        auto fire = [&](int buf, const Panel &p) {
+            if (NL < NW && !loader)
+                return;
+            const __amdgpu_buffer_rsrc_t ra =
+                __builtin_amdgcn_make_buffer_rsrc((void *)p.a, 0, (int)kOutOfRange, kRawBufferFlags);
+            const __amdgpu_buffer_rsrc_t rb =
+                __builtin_amdgcn_make_buffer_rsrc((void *)p.b, 0, p.b_range, kRawBufferFlags);
 #pragma unroll
             for (int j = 0; j < kLoadsA; ++j) {
-                if (!kEvenA && gw * kLoadsA + j >= kInstA)
+                if (!kEvenA && lw * kLoadsA + j >= kInstA)
                     break;
-                const bool ok = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K;
-                buffer_to_lds(ra, &stage[buf][(gw * kLoadsA + j) * kSpanA], ok ? a_off[j] : kOutOfRange, 4 * kVecA);
+                buffer_to_lds(ra, &stage[buf][(lw * kLoadsA + j) * kSpanA], p.oa[j], 4 * kVecA);
             }
-            // The B range ends after B's last element (K-1, N-1): a 4-float
-            // chunk that starts in the last row before column N but runs past
-            // it reads zeros there instead of memory beyond B.
-            const int64_t b_left = 4 * ((int64_t)(g.K - 1 - k0) * g.ldb + (g.N - n0));
-            const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0,
-                (int)(b_left < (int64_t)kOutOfRange ? b_left : (int64_t)kOutOfRange), kRawBufferFlags);
 #pragma unroll
             for (int j = 0; j < kLoadsB; ++j) {
-                if (!kEvenB && gw * kLoadsB + j >= kInstB)
+                if (!kEvenB && lw * kLoadsB + j >= kInstB)
                     break;
-                const bool ok = k0 + b_k[j] < g.K && n0 + b_c[j] < g.N;
-                buffer_to_lds(rb, &stage[buf][kA + (gw * kLoadsB + j) * kSpanB], ok ? b_off[j] : kOutOfRange, 4 * kVecB);
+                buffer_to_lds(rb, &stage[buf][kA + (lw * kLoadsB + j) * kSpanB], p.ob[j], 4 * kVecB);
             }
         };
 
@@ -515,8 +553,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 #pragma unroll
         for (int it = 0; it < S - 1; ++it)
             if (exists(it))
-                issue(it, panel_k(it));
+                fire(it, prepare(panel_k(it)));
         for (int it = 0; it < rounds; ++it) {
+            const bool more = exists(it + S - 1);
+            const Panel next = prepare(panel_k(it + S - 1));
             // Round it has landed once no more than the loads of the rounds
             // after it (up to S-2 of them, kLoads each) are outstanding; the
             // LDS reads of round it-1 are complete as well.  Then the barrier
@@ -526,8 +566,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             else
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
             __builtin_amdgcn_s_barrier();
-            if (exists(it + S - 1))
-                issue((it + S - 1) % S, panel_k(it + S - 1));
+            if (more)
+                fire((it + S - 1) % S, next);
             if (exists(it)) {
 #pragma unroll
                 for (int q = 0; q < BK / 8; ++q) {
@@ -718,8 +758,8 @@ __global__ __launch_bounds__(256) void fill_zero(float *C, int64_t ldc, int M, i
 // Tile shapes: BM x BN output tile, BK = 16 panel depth, WAVES_M x WAVES_N
 // waves each owning a (BM/WAVES_M) x (BN/WAVES_N) block; optional K-split
 // groups and panel-ring depth.
-using Tile256x256W16 = MfmaTile<256, 256, 16, 4, 4>;    // 16 waves of 64 x 64
-using Tile128x128W16 = MfmaTile<128, 128, 16, 4, 4>;    // 16 waves of 32 x 32
+using Tile256x256W16 = MfmaTile<256, 256, 16, 4, 4, 1, 2, 8, 8>;    // 16 waves of 64 x 64, 8 load
+using Tile128x128W16 = MfmaTile<128, 128, 16, 4, 4, 1, 2, 8, 8>;    // 16 waves of 32 x 32, 8 load
 using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;       // 4 waves of 64 x 64
 using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;         // 4 waves of 64 x 32
 using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;         // 4 waves of 32 x 64
@@ -727,8 +767,8 @@ using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;           // 4 waves of 32 x 32
 using Tile64x64S4 = MfmaTile<64, 64, 16, 2, 2, 4>;      // 4 K-split groups of 4 waves
 using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;   // three-buffer panel ring
 using Tile64x64S4R3 = MfmaTile<64, 64, 16, 2, 2, 4, 3>;
-using Tile256x256K32W16 = MfmaTile<256, 256, 32, 4, 4>;  // 32-deep panels
-using Tile128x128K32W16 = MfmaTile<128, 128, 32, 4, 4>;
+using Tile256x256K32W16 = MfmaTile<256, 256, 32, 4, 4, 1, 2, 8, 8>;  // 32-deep panels
+using Tile128x128K32W16 = MfmaTile<128, 128, 32, 4, 4, 1, 2, 8, 8>;
 using Tile64x64K32 = MfmaTile<64, 64, 32, 2, 2>;
 using Tile64x64K32S4 = MfmaTile<64, 64, 32, 2, 2, 4>;
 using Tile64x128K32 = MfmaTile<64, 128, 32, 2, 2>;
