@@ -446,7 +446,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 
     const int total = g.tiles_m * g.tiles_n;
     const int ktiles = (g.K + BK - 1) / BK;
-    const int64_t b_end = (int64_t)(g.K - 1) * g.ldb + g.N;   // floats from B to one past its last element
 
     // Output tile t over K-panels [p_begin, p_end).  A tile whose panels are
     // split between two workgroups (stream-K) adds its partial sum to C,
@@ -472,13 +471,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             for (int j = 0; j < kLoadsA; ++j)
                 p.oa[j] = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K ? a_off[j] : kOutOfRange;
             // When N % 4 != 0 a 4-float chunk can start before column N and
-            // run past it; the B range then ends after B's last element
-            // (K-1, N-1), so in the last row such a chunk reads zeros instead
-            // of memory beyond B.
-            const int64_t b_corner = (int64_t)k0 * g.ldb + n0;
-            const int64_t b_left = 4 * (b_end - b_corner);
-            p.b_range = (g.N & 3) && b_left < (int64_t)kOutOfRange ? (int)b_left : (int)kOutOfRange;
-            p.b = g.B + b_corner;
+            // run past it.  Past column N of rows before K-1 it still reads
+            // inside B; for the panel that holds row K-1 the B range ends
+            // after B's last element (K-1, N-1), so there such a chunk reads
+            // zeros instead of memory beyond B.  That panel's range is under
+            // (BK-1)*ldb + BN floats, which the 32-bit offsets already need.
+            p.b = g.B + ((int64_t)k0 * g.ldb + n0);
+            p.b_range = (g.N & 3) && k0 + BK >= g.K ? 4 * ((g.K - 1 - k0) * (int)g.ldb + (g.N - n0))
+                                                     : (int)kOutOfRange;
 #pragma unroll
             for (int j = 0; j < kLoadsB; ++j)
                 p.ob[j] = k0 + b_k[j] < g.K && n0 + b_c[j] < g.N ? b_off[j] : kOutOfRange;
