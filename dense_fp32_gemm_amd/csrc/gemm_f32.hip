@@ -944,8 +944,10 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    32-deep panels (+1.5 % over 16-deep at 4096^3 and 8192^3 on one box,
 //    equal on another);
 //  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
-//  * at most one 64 x 64 tile per CU with K >= 2048 (skinny shapes):
-//    64 x 64 with K split over four wave groups inside the workgroup;
+//  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
+//    shapes): 64 x 64 with K split over four wave groups inside the
+//    workgroup, 16 waves instead of 4 on the CU (1024^3: 24.6 us against
+//    26.1 for 64-deep panels; 16384 x 64 x 4096: 77 us against 90);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // When a tile count just above a multiple of 256 would leave most CUs idle
@@ -956,8 +958,8 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 // 64 x 64 tiles do better ((2176, 2100, 1000): 93 us against 108).
 // Below the two largest tiles the choices use 32- or 64-deep K-panels: those
 // tiles give each wave few MFMAs per panel, so fewer, deeper panels cut the
-// per-panel barrier, wait and LDS-latency cost (64-deep: +6 to +9 % at 512^3,
-// 1000^3, 1024^3 and 768 x 768 x 2048 with one 64 x 64 tile per CU).  Problems with
+// per-panel barrier, wait and LDS-latency cost (64-deep: +3 to +5 % at 1280^3
+// and 2048 x 1024 x 1024, one or two 64 x 64 tiles per CU).  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
 int select_config(int M, int N, int K, bool dma_ok)
@@ -987,21 +989,22 @@ int select_config(int M, int N, int K, bool dma_ok)
         // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
         return K >= 2048 ? kCfgDma128x128K32W16SK : kCfgDma64x64K32;
     }
-    if (tiles(kCfgDma64x64K32) <= kComputeUnits && K >= 2048)
+    if (tiles(kCfgDma64x64K32) <= kComputeUnits && K > 512)
         return kCfgDma64x64K32S4;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * kComputeUnits)
         return wide;
-    // 64 x 64 tiles.  Up to two per CU, one 4-wave workgroup per SIMD set
-    // leaves each SIMD a single wave, and 64-deep panels halve the per-panel
-    // barrier stalls that then show; with more, several workgroups share a
-    // CU and the smaller 32-deep panels (more resident workgroups) win.
+    // 64 x 64 tiles.  Up to two per CU, the one or two 4-wave workgroups
+    // leave each SIMD one or two waves, and 64-deep panels halve the
+    // per-panel barrier stalls that then show; with more, several workgroups
+    // share a CU and the smaller 32-deep panels (more resident workgroups)
+    // win.
     // Barely more than one tile per CU: stream-K, so the few extra tiles do
     // not double the time.
     const int64_t t64 = tiles(kCfgDma64x64K64);
     if (t64 > kComputeUnits && 4 * t64 <= 5 * kComputeUnits)
         return kCfgDma64x64K64SK;
-    return t64 < 2 * kComputeUnits ? kCfgDma64x64K64 : kCfgDma64x64K32;
+    return t64 <= 2 * kComputeUnits ? kCfgDma64x64K64 : kCfgDma64x64K32;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }

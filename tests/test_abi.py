@@ -134,9 +134,9 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 4096, 4096, 1000, FAKE, 1000, FAKE, ldb, FAKE, 4096)
     assert text.startswith("staged"), text
     # 63 rows of B span more than 2 GiB but 31 do not: the rule's 64-deep
-    # choice for one 64 x 64 tile per CU is replaced, a 32-deep one is kept
+    # choice for two 64 x 64 tiles per CU is replaced, a 32-deep one is kept
     ldb = 10_000_000
-    rc, text = gb.gemm_f32_describe(-1, 1024, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
+    rc, text = gb.gemm_f32_describe(-1, 2048, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
     assert rc == gb.GEMM_F32_OK and text.startswith("staged"), text
     rc, text = gb.gemm_f32_describe(-1, 2048, 2048, 2048, FAKE, 2048, FAKE, ldb, FAKE, 2048)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16 "), text
@@ -150,7 +150,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((4096, 4096, 16384), "dma_256x256x32_w16 "), ((1024, 8192, 8192), "dma_128x128x32_w16 "),
     ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
     ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
-    ((1000, 1000, 1000), "dma_64x64x64 "), ((512, 512, 512), "dma_64x64x64 "),
+    ((1000, 1000, 1000), "dma_64x64x32_ksplit4"), ((512, 512, 1024), "dma_64x64x32_ksplit4"),
+    ((512, 512, 512), "dma_64x64x64 "), ((2048, 1024, 1024), "dma_64x64x64 "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # 272, 400 and 400 tiles: the last round would leave most CUs idle
     ((1025, 1023, 1000), "dma_64x64x64_sk "), ((2560, 2560, 2560), "dma_128x128x32_w16_sk "),
