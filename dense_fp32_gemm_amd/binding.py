@@ -54,6 +54,10 @@ def load() -> ctypes.CDLL:
         lib.gemm_f32_config_info.restype = i
         lib.gemm_f32_describe.argtypes = [i, i, i, i, p, i, p, i, p, i, ctypes.c_char_p, i]
         lib.gemm_f32_describe.restype = i
+        lib.gemm_f32_ws_size.argtypes = [i, i, i]
+        lib.gemm_f32_ws_size.restype = ctypes.c_size_t
+        lib.gemm_f32_ws.argtypes = [i, i, i, p, i, p, i, p, i, p, ctypes.c_size_t, p]
+        lib.gemm_f32_ws.restype = i
         lib.gemm_f32_device_peak.argtypes = [i, ip, ip, ctypes.POINTER(ctypes.c_double)]
         lib.gemm_f32_device_peak.restype = i
         lib.gemm_f32_status_string.argtypes = [i]
@@ -93,6 +97,16 @@ def gemm_f32_config_info(config: int, occupancy: bool = False) -> dict:
     if occupancy:
         out["blocks_per_cu"] = vals[4].value
     return out
+
+
+def gemm_f32_ws_size(M, N, K) -> int:
+    """Workspace bytes the split-K plan for this shape needs (0: not split)."""
+    return load().gemm_f32_ws_size(M, N, K)
+
+
+def gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=0) -> int:
+    """C := A . B, split over K through `workspace` when the shape calls for it."""
+    return load().gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream)
 
 
 def gemm_f32_device_peak(device: int = 0) -> dict:

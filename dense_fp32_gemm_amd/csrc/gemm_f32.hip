@@ -45,6 +45,8 @@ struct GemmArgs {
     int64_t lda, ldb, ldc;
     int M, N, K;
     int tiles_m, tiles_n;
+    int slices;          // K slices of a split-K launch (1 otherwise)
+    int64_t slab;        // floats between two slices' partial products in C
 };
 
 // ---------------------------------------------------------------------------
@@ -351,7 +353,7 @@ __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_bas
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, offset, 0, 0, 0);
 }
 
-template <class T, bool VEC_A, bool VEC_B, bool SK = false>
+template <class T, bool VEC_A, bool VEC_B, bool SK = false, bool SPLIT = false>
 __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -359,6 +361,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
     static_assert(!SK || KS == 1, "stream-K splits K across workgroups, not inside one");
+    static_assert(!(SK && SPLIT), "one way of splitting K across workgroups at a time");
     static_assert(BK == 16 || BK == 32 || BK == 64, "the A layout permutes the 16-byte chunks of 16-, 32- or 64-deep rows");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
     constexpr int kA = BM * BK;                       // floats per A panel
@@ -447,9 +450,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     const int total = g.tiles_m * g.tiles_n;
     const int ktiles = (g.K + BK - 1) / BK;
 
-    // Output tile t over K-panels [p_begin, p_end).  A tile whose panels are
+    // Output tile t over K-panels [p_begin, p_end), written to cbase (C, or
+    // a K slice's partial product in the workspace).  A tile whose panels are
     // split between two workgroups (stream-K) adds its partial sum to C,
     // which holds +0.0 there beforehand; every other tile stores.
+    float *cbase = g.C;
     auto work = [&](int t, int p_begin, int p_end) {
         int tm, tn;
         tile_coords(t, g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
@@ -625,7 +630,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     for (int r = 0; r < 16; ++r) {
                         const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
                         if (row < g.M && col < g.N) {
-                            float *c = &g.C[(int64_t)row * g.ldc + col];
+                            float *c = &cbase[(int64_t)row * g.ldc + col];
                             if (shared)
                                 unsafeAtomicAdd(c, acc[i][j][r]);
                             else
@@ -637,7 +642,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         }
     };
 
-    if (SK) {
+    if (SPLIT) {
+        // Split-K: workgroup w computes tile w % tiles over K slice
+        // w / tiles and stores it into that slice's slab of the workspace.
+        const int slice = blockIdx.x / total;
+        cbase = g.C + (int64_t)slice * g.slab;
+        work(blockIdx.x % total, (int)((int64_t)slice * ktiles / g.slices),
+             (int)((int64_t)(slice + 1) * ktiles / g.slices));
+    } else if (SK) {
         int64_t lo, hi;
         streamk_range(xcd_contiguous(blockIdx.x, gridDim.x), gridDim.x, (int64_t)total * ktiles, lo, hi);
         while (lo < hi) {
@@ -658,6 +670,22 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 // b looks at the start of workgroup range b + 1; if it falls strictly inside
 // a tile, that tile is shared and this block clears it (clipped to M x N).
 // As no two range starts fall inside one tile, each tile is cleared once.
+// Split-K: C = sum of the slices' partial products, added in slice order
+// (slice 0, then 1, ...), so the result does not depend on scheduling.  The
+// workspace holds slice s's M x N product at ws + s*slab, rows N apart.
+__global__ __launch_bounds__(256) void splitk_reduce(const float *ws, int64_t slab, int slices,
+                                                     float *C, int64_t ldc, int M, int N)
+{
+    const int64_t total = (int64_t)M * N;
+    for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        float sum = ws[e];
+        for (int s = 1; s < slices; ++s)
+            sum += ws[s * slab + e];
+        store_c(&C[(e / N) * ldc + e % N], sum);
+    }
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void zero_shared_tiles(GemmArgs g, int workers)
 {
@@ -840,6 +868,10 @@ struct DmaKernel {
 template <class T, bool VA, bool VB>
 struct DmaStreamKKernel {
     static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB, true>;
+};
+template <class T, bool VA, bool VB>
+struct DmaSplitKKernel {
+    static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB, false, true>;
 };
 
 // Stream-K: clear the tiles two workgroups will share, then run the
@@ -1101,13 +1133,93 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     g.K = K;
     g.tiles_m = p.tiles_m;
     g.tiles_n = p.tiles_n;
+    g.slices = 1;
+    g.slab = 0;
     const hipError_t err = kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
+}
+
+// Split-K with a caller's workspace, for problems with few output tiles and
+// a long K: the 64 x 64 K-split tiles run as `slices` independent
+// workgroups per tile, each over a contiguous K slice, writing partial
+// products to the workspace; a second kernel adds them in slice order.
+using TileSplitK = Tile64x64K32S4;
+constexpr int kSplitKMinPanels = 8;     // 32-deep panels per slice, at least
+
+// Slices for this shape, or 1 when split-K does not apply: only while the
+// 64 x 64 tiles fill at most a quarter of the CUs, as many slices as fill
+// them, each at least kSplitKMinPanels panels deep.
+int splitk_slices(int M, int N, int K)
+{
+    if (M < 16 || N < 16 || K <= 0)
+        return 1;
+    const int64_t t = ceil_div(M, TileSplitK::BM) * ceil_div(N, TileSplitK::BN);
+    if (4 * t > kComputeUnits)
+        return 1;
+    int64_t slices = kComputeUnits / t;
+    const int64_t by_depth = ceil_div(K, TileSplitK::BK) / kSplitKMinPanels;
+    if (by_depth < slices)
+        slices = by_depth;
+    return slices >= 2 ? (int)slices : 1;
+}
+
+size_t splitk_bytes(int M, int N, int K)
+{
+    const int slices = splitk_slices(M, N, K);
+    return slices < 2 ? 0 : (size_t)slices * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                  float *C, int ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    Plan p;
+    int rc = make_plan(-1, M, N, K, A, lda, B, ldb, C, ldc, &p);
+    if (rc != GEMM_F32_OK || p.grid == 0 || K == 0)
+        return run(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    const int slices = splitk_slices(M, N, K);
+    const size_t need = splitk_bytes(M, N, K);
+    const ConfigInfo &cfg = kConfigs[kCfgDma64x64K32S4];
+    if (slices < 2 || ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 15u) ||
+        !dma_offsets_fit(cfg, lda, ldb))
+        return run(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    GemmArgs g;
+    g.A = A;
+    g.B = B;
+    g.C = (float *)ws;
+    g.lda = lda;
+    g.ldb = ldb;
+    g.ldc = N;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.tiles_m = (int)ceil_div(M, TileSplitK::BM);
+    g.tiles_n = (int)ceil_div(N, TileSplitK::BN);
+    g.slices = slices;
+    g.slab = (int64_t)M * N;
+    const int grid = g.tiles_m * g.tiles_n * slices;
+    hipError_t err = Launch<TileSplitK, DmaSplitKKernel>::run(g, K % 4 == 0, true, grid, stream);
+    if (err != hipSuccess)
+        return GEMM_F32_ERR_LAUNCH;
+    const int64_t elems = (int64_t)M * N;
+    const int rgrid = (int)(ceil_div(elems, 256) < 4096 ? ceil_div(elems, 256) : 4096);
+    splitk_reduce<<<rgrid, 256, 0, stream>>>((const float *)ws, g.slab, slices, C, ldc, M, N);
+    return hipGetLastError() == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
 }  // namespace
 
 extern "C" {
+
+size_t gemm_f32_ws_size(int M, int N, int K)
+{
+    return M < 0 || N < 0 || K < 0 ? 0 : splitk_bytes(M, N, K);
+}
+
+int gemm_f32_ws(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                float *C, int ldc, void *workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    return run_workspace(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream);
+}
 
 int gemm_f32(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
              float *C, int ldc, hipStream_t stream)

@@ -53,6 +53,8 @@
 #ifndef GEMM_F32_H
 #define GEMM_F32_H
 
+#include <stddef.h>
+
 #include <hip/hip_runtime_api.h>
 
 /* Exported from libgemm_f32.so (the library is built with hidden visibility). */
@@ -96,6 +98,34 @@ GEMM_F32_API int gemm_f32_with_config(int config, int M, int N, int K,
                          const float *B, int ldb,
                          float *C, int ldc,
                          hipStream_t stream);
+
+/*
+ * Split-K with a caller-provided workspace, for problems with few output
+ * tiles and a long K (e.g. 200 x 200 x 20000, whose 64 x 64 tiles would
+ * occupy 16 of the 256 compute units).  The K range is cut into slices that
+ * run as independent workgroups, each writing its partial product into the
+ * workspace; a second kernel then adds the slices in slice order (0, 1, ...)
+ * into C, so the result is deterministic (and bit-exact whenever every
+ * partial sum is representable, as with the other entry points).
+ *
+ * gemm_f32_ws_size() returns the workspace bytes the split plan for this
+ * shape needs, or 0 when the shape is not split (enough tiles already, or K
+ * too short).  gemm_f32_ws() computes C := A . B like gemm_f32(); it uses
+ * the split plan when gemm_f32_ws_size(M, N, K) > 0, `workspace` is a
+ * 16-byte aligned device buffer of at least that many bytes that overlaps
+ * none of A, B and C, and the leading dimensions allow 32-bit panel
+ * offsets; otherwise it runs exactly what gemm_f32() runs and leaves the
+ * workspace untouched.  The caller owns the workspace; its contents on
+ * return are unspecified.  Validation and return codes are gemm_f32()'s.
+ * Calls that share a workspace must not run concurrently.
+ */
+GEMM_F32_API size_t gemm_f32_ws_size(int M, int N, int K);
+GEMM_F32_API int gemm_f32_ws(int M, int N, int K,
+                             const float *A, int lda,
+                             const float *B, int ldb,
+                             float *C, int ldc,
+                             void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Number of kernel configurations, and the name of one ("" if unknown). */
 GEMM_F32_API int gemm_f32_num_configs(void);

@@ -198,3 +198,22 @@ def test_streamk_grid_is_one_worker_per_compute_unit():
     # fewer tiles than compute units: one worker per tile, nothing shared
     rc, text = gb.gemm_f32_describe(cfg, 300, 300, 1000, FAKE, 1000, FAKE, 300, FAKE, 300)
     assert rc == gb.GEMM_F32_OK and "tiles=5x5 grid=25 " in text, text
+
+
+def test_split_k_workspace_size():
+    # 200 x 200: 16 tiles of 64 x 64 -> 16 slices of a 20000-deep K
+    assert gb.gemm_f32_ws_size(200, 200, 20000) == 16 * 200 * 200 * 4
+    # slices also limited by K: 625 panels of 32 -> at most 78 slices of 8 panels
+    assert gb.gemm_f32_ws_size(64, 64, 1024) == 4 * 64 * 64 * 4
+    # enough tiles, too short a K, tiny or invalid shapes: not split
+    for shape in [(8192, 8192, 8192), (2048, 2048, 2048), (1024, 1024, 8192), (64, 64, 256),
+                  (200, 200, 0), (8, 8, 100000), (-1, 200, 20000)]:
+        assert gb.gemm_f32_ws_size(*shape) == 0, shape
+
+
+def test_split_k_entry_point_validates_like_gemm_f32():
+    ws = 1 << 20
+    assert gb.gemm_f32_ws(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, FAKE, ws, 0) == gb.GEMM_F32_ERR_DIM
+    assert gb.gemm_f32_ws(5, 9, 8, FAKE, 7, FAKE, 9, FAKE, 9, FAKE, ws, 0) == gb.GEMM_F32_ERR_LD
+    assert gb.gemm_f32_ws(5, 9, 8, 0, 8, FAKE, 9, FAKE, 9, FAKE, ws, 0) == gb.GEMM_F32_ERR_NULL
+    assert gb.gemm_f32_ws(0, 9, 8, 0, 8, 0, 9, 0, 9, 0, 0, 0) == gb.GEMM_F32_OK

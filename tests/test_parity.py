@@ -416,3 +416,58 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, eager)
+
+
+# ---------------------------------------------------------------------------
+# Split-K through a caller's workspace (few tiles, long K).
+# ---------------------------------------------------------------------------
+def gpu_gemm_ws(A, B, dev, ws_bytes=None, ldc_pad=0):
+    M, K = A.shape
+    N = B.shape[1]
+    need = gb.gemm_f32_ws_size(M, N, K)
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    ldc = N + ldc_pad
+    dC = torch.full((M * ldc + 1,), float("nan"), device=dev)
+    ws = torch.full((max(1, ws_bytes // 4),), float("nan"), device=dev)
+    say(f"gemm_f32_ws M={M} N={N} K={K} workspace {ws_bytes} of {need} bytes")
+    rc = gb.gemm_f32_ws(M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dC.data_ptr(), ldc,
+                        ws.data_ptr(), ws_bytes, torch.cuda.current_stream().cuda_stream)
+    assert rc == gb.GEMM_F32_OK, gb.gemm_f32_status_string(rc)
+    torch.cuda.synchronize()
+    full = dC.cpu().numpy()
+    return np.ascontiguousarray(full[:M * ldc].reshape(M, ldc)[:, :N]), full, ws.cpu().numpy(), need
+
+
+SPLITK = [(200, 200, 20000), (130, 70, 5000), (64, 300, 3000), (17, 1000, 4096)]
+
+
+@pytest.mark.parametrize("shape", SPLITK, ids=lambda s: "x".join(map(str, s)))
+def test_split_k_bit_exact_and_padding_kept(dev, shape):
+    A, B = operands("quarter", *shape)
+    got, full, _, need = gpu_gemm_ws(A, B, dev, ldc_pad=3)
+    assert need > 0
+    assert_bit_exact(got, oracle.gemm(A, B), f"{shape} split-K")
+    M, N, _ = shape
+    body = full[:M * (N + 3)].reshape(M, N + 3)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[-1])
+
+
+def test_split_k_uniform_within_tolerance_and_deterministic(dev):
+    A, B = operands("uniform", 200, 200, 20000)
+    first, _, _, _ = gpu_gemm_ws(A, B, dev)
+    assert_close(first, oracle.gemm(A, B), "200x200x20000 split-K")
+    for _ in range(2):
+        again, _, _, _ = gpu_gemm_ws(A, B, dev)
+        assert_bit_exact(again, first, "split-K repeat")
+
+
+def test_split_k_short_workspace_runs_the_plain_path(dev):
+    """Too small a workspace: the call is gemm_f32's and the workspace is
+    not touched."""
+    A, B = operands("quarter", 130, 70, 5000)
+    got, _, ws, need = gpu_gemm_ws(A, B, dev, ws_bytes=1 << 12)
+    assert need > (1 << 12)
+    assert_bit_exact(got, oracle.gemm(A, B), "short workspace")
+    assert np.isnan(ws).all()
