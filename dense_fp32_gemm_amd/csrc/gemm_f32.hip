@@ -386,6 +386,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     static_assert(kA % kSpanA == 0 && kB % kSpanB == 0, "panel split");
     constexpr int S = T::kStages;
     constexpr int kLoads = kLoadsA + kLoadsB;         // per wave per round
+    // The 128-bit C epilogue stages kWaveM x BN floats in the panel buffers.
+    // It pays where writing C weighs most, the 4-wave tiles chosen for short
+    // K; on the 16-wave tiles of long-K problems it measured 0.4-0.8 % slower.
+    constexpr bool kBandEpilogue = KS == 1 && NW == 4 && T::kWaveM * BN <= S * kStage;
     static_assert(S >= 2 && (S - 2) * kLoads <= 63, "vmcnt range");
     static_assert(S == 2 || (kEvenA && kEvenB), "partial vmcnt waits need equal per-wave load counts");
     static_assert(KS * S * kStage * 4 <= 160 * 1024, "LDS budget");
@@ -456,6 +460,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     // which holds +0.0 there beforehand; every other tile stores.
     float *cbase = g.C;
     auto work = [&](int t, int p_begin, int p_end) {
+        const bool c_vec = ((uintptr_t)cbase & 15u) == 0 && (g.ldc & 3) == 0;
         int tm, tn;
         tile_coords(t, g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
         const int m0 = tm * BM;
@@ -620,6 +625,41 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         }
 
         const bool shared = SK && (p_begin != 0 || p_end != ktiles);
+        if (kBandEpilogue && !shared && c_vec && m0 + BM <= g.M && n0 + BN <= g.N) {
+            // Whole tile, 16-byte aligned rows of C: stage one band of
+            // kWaveM rows at a time through the (now idle) panel buffers and
+            // write C with 128-bit stores of whole rows instead of one
+            // 32-bit store per accumulator element (+3.5 to +7 % on
+            // 8192 x 8192 x 128, whose time is dominated by writing C).  The
+            // band is [kWaveM][BN]; rows with bit 2 set have their columns
+            // swapped in 32-float halves, so the two lane halves of an
+            // accumulator write (rows 4 apart) fall on different banks.
+            float *band = &lds[0][0][0];
+            for (int p = 0; p < T::WAVES_M; ++p) {
+                if (wave_m == p) {
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+#pragma unroll
+                            for (int r = 0; r < 16; ++r) {
+                                const int lr = i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                                const int lc = (wave_n * T::kWaveN + j * 32 + li) ^ ((lr & 4) ? 32 : 0);
+                                band[lr * BN + lc] = acc[i][j][r];
+                            }
+                }
+                __syncthreads();
+                constexpr int kRowChunks = BN / 4;
+                for (int e = tid; e < T::kWaveM * kRowChunks; e += T::kThreads) {
+                    const int lr = e / kRowChunks, c4 = e % kRowChunks;
+                    const f32x4 v = *reinterpret_cast<const f32x4 *>(&band[lr * BN + ((4 * c4) ^ ((lr & 4) ? 32 : 0))]);
+                    float *dst = &cbase[(int64_t)(m0 + p * T::kWaveM + lr) * g.ldc + n0 + 4 * c4];
+                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
+                }
+                __syncthreads();
+            }
+            return;
+        }
         if (group == 0) {
 #pragma unroll
             for (int i = 0; i < FM; ++i) {
