@@ -471,12 +471,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         // loads (loader waves only).
         struct Panel {
             const float *a, *b;          // panel corners
-            int b_range;                 // bytes of B from b on
+            int a_range, b_range;        // bytes of A from a on, of B from b on
             uint32_t oa[kLoadsA], ob[kLoadsB];
         };
         auto prepare = [&](int k0) {
             Panel p;
             p.a = g.A + ((int64_t)m0 * g.lda + k0);
+            // Likewise for A when K % 4 != 0: in the panel holding column
+            // K-1 a chunk can run past it (the elements it picks up there are
+            // cleared in LDS before use, see clear_a_tail); for the tile
+            // holding row M-1 that panel's A range ends after A's last
+            // element.
+            p.a_range = (g.K & 3) && k0 + BK >= g.K && m0 + BM >= g.M
+                            ? 4 * ((g.M - 1 - m0) * (int)g.lda + (g.K - k0))
+                            : (int)kOutOfRange;
 #pragma unroll
             for (int j = 0; j < kLoadsA; ++j)
                 p.oa[j] = m0 + a_r[j] < g.M && k0 + a_k[j] < g.K ? a_off[j] : kOutOfRange;
@@ -498,7 +506,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             if (NL < NW && !loader)
                 return;
             const __amdgpu_buffer_rsrc_t ra =
-                __builtin_amdgcn_make_buffer_rsrc((void *)p.a, 0, (int)kOutOfRange, kRawBufferFlags);
+                __builtin_amdgcn_make_buffer_rsrc((void *)p.a, 0, p.a_range, kRawBufferFlags);
             const __amdgpu_buffer_rsrc_t rb =
                 __builtin_amdgcn_make_buffer_rsrc((void *)p.b, 0, p.b_range, kRawBufferFlags);
 #pragma unroll
@@ -559,6 +567,26 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         const int rounds = (npanels + KS - 1) / KS;
         auto exists = [&](int it) { return it < rounds && (KS == 1 || it * KS + group < npanels); };
         auto panel_k = [&](int it) { return (p_begin + it * KS + group) * BK; };
+        // With 128-bit A loads and K % 4 != 0, the chunk of each A row that
+        // holds column K-1 also brings 1 to 3 elements past it (the row's
+        // padding or the next row's first elements), which would meet B's
+        // zero-filled rows >= K: harmless if finite, NaN if not.  Once the
+        // panel holding column K-1 (round tail_round of group tail_group) is
+        // in LDS, those elements are set to +0.0, followed by one barrier.
+        const bool a_tail = VEC_A && (g.K & 3) && p_end == ktiles;
+        const int tail_round = (ktiles - 1 - p_begin) / KS;
+        const int tail_group = (ktiles - 1 - p_begin) % KS;
+        auto clear_a_tail = [&](int buf) {
+            const int valid = g.K - (ktiles - 1) * BK;       // columns of the panel below K
+            const int chunk = valid / 4, first = valid % 4;
+            constexpr int NT = NW * kWaveSize;                // threads of the group
+            const int gt = tid - group * NT;
+            for (int e = gt; e < BM * 4; e += NT) {
+                const int r = e / 4, x = e % 4;
+                if (x >= first)
+                    stage[buf][r * BK + 4 * (chunk ^ swz_a<BK>(r)) + x] = 0.f;
+            }
+        };
         // Rounds it+1 .. it+S-1 are in flight while round it is computed.
 #pragma unroll
         for (int it = 0; it < S - 1; ++it)
@@ -578,6 +606,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             __builtin_amdgcn_s_barrier();
             if (more)
                 fire((it + S - 1) % S, next);
+            if (a_tail && it == tail_round) {
+                if (group == tail_group)
+                    clear_a_tail(it % S);
+                __syncthreads();
+            }
             if (exists(it)) {
 #pragma unroll
                 for (int q = 0; q < BK / 8; ++q) {
@@ -1137,11 +1170,12 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     if (kConfigs[c].dma) {
         // Direct-to-LDS loads move 16 bytes from any 4-byte aligned address
         // (checked on gfx950 together with the per-dword range check).  A
-        // 4-float chunk of an A row never crosses column K when K % 4 == 0.  A
         // chunk of B that crosses column N only feeds C columns >= N, which
-        // are never stored, and the panel's buffer range ends at B's last
-        // element, so nothing beyond B is read.
-        plan->vec_a = K % 4 == 0;
+        // are never stored; a chunk of A that crosses column K has the
+        // elements past it cleared in LDS before use.  The panels' buffer
+        // ranges end at A's and B's last elements, so nothing beyond them is
+        // read.
+        plan->vec_a = true;
         plan->vec_b = true;
     } else {
         plan->vec_a = aligned16(A) && lda % 4 == 0 && K % 4 == 0;
@@ -1237,7 +1271,7 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     g.slices = slices;
     g.slab = (int64_t)M * N;
     const int grid = g.tiles_m * g.tiles_n * slices;
-    hipError_t err = Launch<TileSplitK, DmaSplitKKernel>::run(g, K % 4 == 0, true, grid, stream);
+    hipError_t err = Launch<TileSplitK, DmaSplitKKernel>::run(g, true, true, grid, stream);
     if (err != hipSuccess)
         return GEMM_F32_ERR_LAUNCH;
     const int64_t elems = (int64_t)M * N;

@@ -103,14 +103,13 @@ def test_describe():
     assert rc == gb.GEMM_F32_ERR_DIM and text.startswith("invalid")
     rc, text = gb.gemm_f32_describe(-1, 8192, 8192, 8192, FAKE, 8192, FAKE, 8192, FAKE, 8192)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma") and "load_a=x4 load_b=x4" in text
-    # direct-to-LDS loads: 128-bit from any 4-byte aligned address; A only
-    # when K % 4 == 0 (its chunks must not cross column K), B always
+    # direct-to-LDS loads: 128-bit from any 4-byte aligned address, for any K
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, 1023, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and "load_a=x4 load_b=x4" in text
     rc, text = gb.gemm_f32_describe(-1, 512, 512, 512, FAKE + 4, 515, FAKE + 8, 517, FAKE, 512)
     assert text.startswith("dma") and "load_a=x4 load_b=x4" in text, text
     rc, text = gb.gemm_f32_describe(-1, 512, 512, 1001, FAKE, 1001, FAKE, 512, FAKE, 512)
-    assert text.startswith("dma") and "load_a=x1 load_b=x4" in text, text
+    assert text.startswith("dma") and "load_a=x4 load_b=x4" in text, text
     rc, text = gb.gemm_f32_describe(-1, 1, 1, 1, FAKE, 1, FAKE, 1, FAKE, 1)
     assert rc == gb.GEMM_F32_OK and text.startswith("valu")
     # the register-staged kernel keeps 16-byte alignment for its 128-bit loads

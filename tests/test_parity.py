@@ -471,3 +471,16 @@ def test_split_k_short_workspace_runs_the_plain_path(dev):
     assert need > (1 << 12)
     assert_bit_exact(got, oracle.gemm(A, B), "short workspace")
     assert np.isnan(ws).all()
+
+
+@pytest.mark.parametrize("config", [c for c in CONFIGS if gb.gemm_f32_config_name(c).startswith("dma")],
+                         ids=[n for n in CONFIG_IDS if n.startswith("dma")])
+def test_a_chunks_crossing_column_k_are_cleared(dev, config):
+    """K % 4 != 0 with NaN in A's row padding (and after A's last element):
+    the 128-bit A chunk holding column K-1 picks those up in LDS, where they
+    must be cleared before they meet B's zero rows (NaN * 0 would be NaN)."""
+    for M, N, K in ((130, 200, 77), (300, 128, 131), (64, 64, 5)):
+        A, B = operands("quarter", M, N, K)
+        for pad, off in (((0, 0, 0), (0, 0, 0)), ((3, 0, 0), (0, 0, 0)), ((1, 2, 0), (3, 1, 0))):
+            got, _ = gpu_gemm(A, B, config, dev, pad=pad, offset=off)
+            assert_bit_exact(got, oracle.gemm(A, B), f"{(M, N, K)} pad {pad} off {off}")
