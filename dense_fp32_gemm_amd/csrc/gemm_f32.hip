@@ -310,13 +310,15 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 // Matrix-core kernel with direct-to-LDS operand loads.
 //
 // gfx950 buffer loads can write their result straight into LDS
-// (buffer_load_dword[x4] ... lds): lane l of a wave deposits its 4 or 16
-// bytes at LDS base + l*size, so one wave instruction fills 256 B or 1 KB of
-// LDS with no VGPR staging and no ds_write.  Which global element lands in
-// which LDS slot is chosen through the per-lane global offset, which is how
-// the bank-conflict-avoiding layouts below are produced.  A buffer offset
-// outside the resource's range reads as zero, so ragged rows, columns and
-// K-tails are zero-filled by pointing their lanes at an out-of-range offset.
+// (buffer_load_dwordx4 ... lds): lane l of a wave deposits its 16 bytes at
+// LDS base + 16*l, so one wave instruction fills 1 KB of LDS with no VGPR
+// staging and no ds_write.  The global side only needs 4-byte alignment, so
+// every operand takes this path.  Which global element lands in which LDS
+// slot is chosen through the per-lane global offset, which is how the
+// bank-conflict-avoiding layouts below are produced.  A buffer offset
+// outside the resource's range reads as zero (dword by dword), so ragged
+// rows, columns and K-tails are zero-filled by pointing their lanes at an
+// out-of-range offset.
 //
 // LDS layouts (per panel, BK = 16, 32 or 64):
 //  * A: [BM][BK] floats, the BK/4 16-byte chunks of row r permuted by
@@ -344,16 +346,15 @@ __device__ inline int swz_a(int r)
     return BK == 16 ? (r >> 2) & 3 : BK == 32 ? (r ^ (r >> 3)) & 7 : r & 15;
 }
 
-__device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_base, uint32_t offset, int bytes)
+// One wave instruction: lane l's 16 bytes at buffer offset `offset` land at
+// lds_base + 16*l.
+__device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_base, uint32_t offset)
 {
     auto *dst = (__attribute__((address_space(3))) void *)lds_base;
-    if (bytes == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, offset, 0, 0, 0);
-    else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, offset, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, offset, 0, 0, 0);
 }
 
-template <class T, bool VEC_A, bool VEC_B, bool SK = false, bool SPLIT = false>
+template <class T, bool SK = false, bool SPLIT = false>
 __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -367,7 +368,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int kA = BM * BK;                       // floats per A panel
     constexpr int kB = BK * BN;                       // floats per B panel
     constexpr int kStage = kA + kB;
-    constexpr int kVecA = VEC_A ? 4 : 1, kVecB = VEC_B ? 4 : 1;
+    constexpr int kVecA = 4, kVecB = 4;               // floats per lane per load (16 bytes)
     constexpr int kSpanA = kWaveSize * kVecA;         // floats one instruction moves
     constexpr int kSpanB = kWaveSize * kVecB;
     // Load instructions per panel, dealt in order to the group's first NL
@@ -513,13 +514,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             for (int j = 0; j < kLoadsA; ++j) {
                 if (!kEvenA && lw * kLoadsA + j >= kInstA)
                     break;
-                buffer_to_lds(ra, &stage[buf][(lw * kLoadsA + j) * kSpanA], p.oa[j], 4 * kVecA);
+                buffer_to_lds(ra, &stage[buf][(lw * kLoadsA + j) * kSpanA], p.oa[j]);
             }
 #pragma unroll
             for (int j = 0; j < kLoadsB; ++j) {
                 if (!kEvenB && lw * kLoadsB + j >= kInstB)
                     break;
-                buffer_to_lds(rb, &stage[buf][kA + (lw * kLoadsB + j) * kSpanB], p.ob[j], 4 * kVecB);
+                buffer_to_lds(rb, &stage[buf][kA + (lw * kLoadsB + j) * kSpanB], p.ob[j]);
             }
         };
 
@@ -573,7 +574,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         // zero-filled rows >= K: harmless if finite, NaN if not.  Once the
         // panel holding column K-1 (round tail_round of group tail_group) is
         // in LDS, those elements are set to +0.0, followed by one barrier.
-        const bool a_tail = VEC_A && (g.K & 3) && p_end == ktiles;
+        const bool a_tail = (g.K & 3) && p_end == ktiles;
         const int tail_round = (ktiles - 1 - p_begin) / KS;
         const int tail_group = (ktiles - 1 - p_begin) % KS;
         auto clear_a_tail = [&](int buf) {
@@ -929,22 +930,30 @@ struct Launch {
     }
 };
 
-// Adapters so one launcher serves both matrix-core kernels.
+// Adapter giving the register-staged kernel the launcher's interface.
 template <class T, bool VA, bool VB>
 struct PlainKernel {
     static constexpr auto fn = gemm_f32_mfma<T, VA, VB>;
 };
-template <class T, bool VA, bool VB>
-struct DmaKernel {
-    static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB>;
-};
-template <class T, bool VA, bool VB>
-struct DmaStreamKKernel {
-    static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB, true>;
-};
-template <class T, bool VA, bool VB>
-struct DmaSplitKKernel {
-    static constexpr auto fn = gemm_f32_mfma_dma<T, VA, VB, false, true>;
+
+// The direct-to-LDS kernel has one instance per tile and mode: it loads 16
+// bytes per lane from any 4-byte aligned operand, so the load-width flags
+// of the plan do not apply to it.
+template <class T, bool SK = false, bool SPLIT = false>
+struct LaunchDma {
+    static hipError_t run(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
+    {
+        hipLaunchKernelGGL((gemm_f32_mfma_dma<T, SK, SPLIT>), dim3(grid), dim3(T::kThreads), 0, s, g);
+        return hipGetLastError();
+    }
+    static int occupancy()
+    {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_f32_mfma_dma<T, SK, SPLIT>, T::kThreads, 0) !=
+            hipSuccess)
+            return -1;
+        return n;
+    }
 };
 
 // Stream-K: clear the tiles two workgroups will share, then run the
@@ -958,7 +967,7 @@ hipError_t launch_streamk(const GemmArgs &g, bool va, bool vb, int grid, hipStre
         if (e != hipSuccess)
             return e;
     }
-    return Launch<T, DmaStreamKKernel>::run(g, va, vb, grid, s);
+    return LaunchDma<T, true>::run(g, va, vb, grid, s);
 }
 
 hipError_t launch_valu(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
@@ -984,45 +993,52 @@ struct ConfigInfo {
     bool streamk;                // one worker per CU over all tiles' K-panels
 };
 
-template <class T, template <class, bool, bool> class Kernel>
-constexpr ConfigInfo config(const char *name, bool dma)
+template <class T>
+constexpr ConfigInfo config_staged(const char *name)
 {
-    return {name, T::BM, T::BN, T::BK, T::kThreads, dma, &Launch<T, Kernel>::run,
-            &Launch<T, Kernel>::occupancy, false};
+    return {name, T::BM, T::BN, T::BK, T::kThreads, false, &Launch<T, PlainKernel>::run,
+            &Launch<T, PlainKernel>::occupancy, false};
+}
+
+template <class T>
+constexpr ConfigInfo config_dma(const char *name)
+{
+    return {name, T::BM, T::BN, T::BK, T::kThreads, true, &LaunchDma<T>::run, &LaunchDma<T>::occupancy,
+            false};
 }
 
 template <class T>
 constexpr ConfigInfo config_streamk(const char *name)
 {
     return {name, T::BM, T::BN, T::BK, T::kThreads, true, &launch_streamk<T>,
-            &Launch<T, DmaStreamKKernel>::occupancy, true};
+            &LaunchDma<T, true>::occupancy, true};
 }
 
 // Indexed by ConfigId.
 const ConfigInfo kConfigs[kNumConfigs] = {
     {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu, false},
-    config<Tile256x256W16, DmaKernel>("dma_256x256x16_w16", true),
-    config<Tile128x128W16, DmaKernel>("dma_128x128x16_w16", true),
-    config<Tile128x128, DmaKernel>("dma_128x128x16", true),
-    config<Tile128x64, DmaKernel>("dma_128x64x16", true),
-    config<Tile64x128, DmaKernel>("dma_64x128x16", true),
-    config<Tile64x64, DmaKernel>("dma_64x64x16", true),
-    config<Tile64x64S4, DmaKernel>("dma_64x64x16_ksplit4", true),
-    config<Tile128x128R3, DmaKernel>("dma_128x128x16_ring3", true),
-    config<Tile64x64S4R3, DmaKernel>("dma_64x64x16_ksplit4_ring3", true),
-    config<Tile128x128, PlainKernel>("staged_128x128x16", false),
-    config<Tile64x64, PlainKernel>("staged_64x64x16", false),
-    config<Tile256x256K32W16, DmaKernel>("dma_256x256x32_w16", true),
-    config<Tile128x128K32W16, DmaKernel>("dma_128x128x32_w16", true),
-    config<Tile64x64K32, DmaKernel>("dma_64x64x32", true),
-    config<Tile64x64K32S4, DmaKernel>("dma_64x64x32_ksplit4", true),
-    config<Tile64x128K32, DmaKernel>("dma_64x128x32", true),
-    config<Tile128x64K32, DmaKernel>("dma_128x64x32", true),
-    config<Tile128x128K32, DmaKernel>("dma_128x128x32", true),
+    config_dma<Tile256x256W16>("dma_256x256x16_w16"),
+    config_dma<Tile128x128W16>("dma_128x128x16_w16"),
+    config_dma<Tile128x128>("dma_128x128x16"),
+    config_dma<Tile128x64>("dma_128x64x16"),
+    config_dma<Tile64x128>("dma_64x128x16"),
+    config_dma<Tile64x64>("dma_64x64x16"),
+    config_dma<Tile64x64S4>("dma_64x64x16_ksplit4"),
+    config_dma<Tile128x128R3>("dma_128x128x16_ring3"),
+    config_dma<Tile64x64S4R3>("dma_64x64x16_ksplit4_ring3"),
+    config_staged<Tile128x128>("staged_128x128x16"),
+    config_staged<Tile64x64>("staged_64x64x16"),
+    config_dma<Tile256x256K32W16>("dma_256x256x32_w16"),
+    config_dma<Tile128x128K32W16>("dma_128x128x32_w16"),
+    config_dma<Tile64x64K32>("dma_64x64x32"),
+    config_dma<Tile64x64K32S4>("dma_64x64x32_ksplit4"),
+    config_dma<Tile64x128K32>("dma_64x128x32"),
+    config_dma<Tile128x64K32>("dma_128x64x32"),
+    config_dma<Tile128x128K32>("dma_128x128x32"),
     config_streamk<Tile64x64K32>("dma_64x64x32_sk"),
     config_streamk<Tile128x128K32W16>("dma_128x128x32_w16_sk"),
     config_streamk<Tile256x256W16>("dma_256x256x16_w16_sk"),
-    config<Tile64x64K64, DmaKernel>("dma_64x64x64", true),
+    config_dma<Tile64x64K64>("dma_64x64x64"),
     config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
 };
 
@@ -1271,7 +1287,7 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     g.slices = slices;
     g.slab = (int64_t)M * N;
     const int grid = g.tiles_m * g.tiles_n * slices;
-    hipError_t err = Launch<TileSplitK, DmaSplitKKernel>::run(g, true, true, grid, stream);
+    hipError_t err = LaunchDma<TileSplitK, false, true>::run(g, true, true, grid, stream);
     if (err != hipSuccess)
         return GEMM_F32_ERR_LAUNCH;
     const int64_t elems = (int64_t)M * N;
