@@ -877,6 +877,8 @@ using Tile64x128K32 = MfmaTile<64, 128, 32, 2, 2>;
 using Tile128x64K32 = MfmaTile<128, 64, 32, 2, 2>;
 using Tile128x128K32 = MfmaTile<128, 128, 32, 2, 2>;
 using Tile64x64K64 = MfmaTile<64, 64, 64, 2, 2>;         // 64-deep panels
+// 2 K-split groups of 8 waves of 32 x 64, 4 of them loading
+using Tile128x128K32S2 = MfmaTile<128, 128, 32, 4, 2, 2, 2, 8, 4>;
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -903,6 +905,7 @@ enum ConfigId {
     kCfgDma256x256W16SK,
     kCfgDma64x64K64,
     kCfgDma64x64K64SK,
+    kCfgDma128x128K32S2,
     kNumConfigs
 };
 
@@ -1040,6 +1043,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_streamk<Tile256x256W16>("dma_256x256x16_w16_sk"),
     config_dma<Tile64x64K64>("dma_64x64x64"),
     config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
+    config_dma<Tile128x128K32S2>("dma_128x128x32_ksplit2"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1064,7 +1068,10 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64,
 //    32-deep panels (+1.5 % over 16-deep at 4096^3 and 8192^3 on one box,
 //    equal on another);
-//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves of 32 x 32;
+//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves in two K-split
+//    groups of 8 waves of 32 x 64 (+0.7 to +3.6 % over one group of 16
+//    waves of 32 x 32: 2048^3, 2048 x 2048 x 4096, 4096 x 2048 x 2048,
+//    1024 x 8192 x 8192);
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
 //    shapes): 64 x 64 with K split over four wave groups inside the
 //    workgroup, 16 waves instead of 4 on the CU (1024^3: 24.6 us against
@@ -1105,7 +1112,7 @@ int select_config(int M, int N, int K, bool dma_ok)
         return unbalanced(kCfgDma256x256K32W16) ? kCfgDma256x256W16SK : kCfgDma256x256K32W16;
     if (tiles(kCfgDma128x128K32W16) >= kComputeUnits) {
         if (!unbalanced(kCfgDma128x128K32W16))
-            return kCfgDma128x128K32W16;
+            return kCfgDma128x128K32S2;
         // Stream-K's extra launch and split-tile passes pay off over a long
         // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
         return K >= 2048 ? kCfgDma128x128K32W16SK : kCfgDma64x64K32;

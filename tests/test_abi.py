@@ -138,15 +138,15 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 2048, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
     assert rc == gb.GEMM_F32_OK and text.startswith("staged"), text
     rc, text = gb.gemm_f32_describe(-1, 2048, 2048, 2048, FAKE, 2048, FAKE, ldb, FAKE, 2048)
-    assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16 "), text
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_ksplit2 "), text
     k64 = gb.config_names().index("dma_64x64x64")
     rc, _ = gb.gemm_f32_describe(k64, 1024, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
     assert rc == gb.GEMM_F32_ERR_CONFIG
 
 
 @pytest.mark.parametrize("shape,name", [
-    ((8192, 8192, 8192), "dma_256x256x32_w16 "), ((2048, 2048, 2048), "dma_128x128x32_w16 "),
-    ((4096, 4096, 16384), "dma_256x256x32_w16 "), ((1024, 8192, 8192), "dma_128x128x32_w16 "),
+    ((8192, 8192, 8192), "dma_256x256x32_w16 "), ((2048, 2048, 2048), "dma_128x128x32_ksplit2 "),
+    ((4096, 4096, 16384), "dma_256x256x32_w16 "), ((1024, 8192, 8192), "dma_128x128x32_ksplit2 "),
     ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
     ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
     ((1000, 1000, 1000), "dma_64x64x32_ksplit4"), ((512, 512, 1024), "dma_64x64x32_ksplit4"),
