@@ -129,11 +129,24 @@ def cpu_baseline(M, N, K, budget_s=12.0):
         if dt > budget_s / 4 or rows >= M:
             break
         rows = min(M, int(rows * max(2.0, budget_s / 2 / max(dt, 1e-3))))
+    cores = oracle.threads()
+    # One core: the full 512^3 product (about 0.3 s), for comparison with
+    # single-threaded CPU figures.
+    A1, B1 = inputs.uniform(512, 512, 512)
+    oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.gemm(A1, B1)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(cores)
     return {
         "value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOPS",
-        "cores": oracle.threads(), "kind": "oracle",
+        "cores": cores, "kind": "oracle",
         "sample": f"first {rows} of {M} rows of C ({M}x{N}x{K} uniform operands), "
                   f"{dt:.1f} s, binary64 accumulation, OpenMP over rows",
+        "single_core": {"value": 2.0 * 512 ** 3 / dt1 / 1e12, "unit": "TFLOPS",
+                        "sample": f"full 512x512x512 product, 1 thread, {dt1:.2f} s"},
     }
 
 

@@ -77,6 +77,8 @@ class Oracle:
         lib.oracle_gemm_f32_at.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_threads.restype = None
         self._lib = lib
         self.path = path
 
@@ -125,6 +127,10 @@ class Oracle:
         """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all cores)."""
         return self._lib.oracle_threads()
 
+    def set_threads(self, n: int) -> None:
+        """Use n OpenMP threads from now on (the results do not depend on it)."""
+        self._lib.oracle_set_threads(int(n))
+
 
 _default: Oracle | None = None
 
@@ -149,3 +155,7 @@ def gemm_at(A, B, rows, cols):
 
 def threads() -> int:
     return load().threads()
+
+
+def set_threads(n: int) -> None:
+    load().set_threads(n)

@@ -93,3 +93,11 @@ int oracle_threads(void)
 {
     return omp_get_max_threads();
 }
+
+/* Sets that thread count (n >= 1); rows are still split the same way, so
+ * the results do not change. */
+void oracle_set_threads(int n)
+{
+    if (n >= 1)
+        omp_set_num_threads(n);
+}

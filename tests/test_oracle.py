@@ -239,6 +239,21 @@ def test_thread_count_does_not_change_results():
     assert bytes.fromhex(out) == here.tobytes()
 
 
+def test_set_threads():
+    A, B = inputs.uniform(97, 61, 300)
+    before = ORC.threads()
+    try:
+        ORC.set_threads(1)
+        assert ORC.threads() == 1
+        one = ORC.gemm(A, B)
+        ORC.set_threads(3)
+        assert ORC.threads() == 3
+        assert ORC.gemm(A, B).tobytes() == one.tobytes()
+    finally:
+        ORC.set_threads(before)
+    assert ORC.threads() == before
+
+
 # ---------------------------------------------------------------------------
 # Planted mistakes: each mutant of oracle.c must fail at least one pin
 # ---------------------------------------------------------------------------
