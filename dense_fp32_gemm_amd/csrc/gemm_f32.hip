@@ -3,17 +3,23 @@
 // C[M x N] = A[M x K] . B[K x N], row-major binary32 (the product of the
 // UIUC ECE408 Lecture 12 final-project page, project_template.cu section 2).
 //
-// Two kernel families:
+// Kernels:
 //
-//  * gemm_f32_mfma<Tile, VEC_A, VEC_B>: one workgroup per BM x BN tile of C.
-//    K is walked in BK-deep panels that are staged global -> VGPR -> LDS
-//    with two LDS buffers, so the next panel is fetched while the matrix
-//    cores work on the current one (one barrier per panel).  Each wave owns a
-//    (BM/WAVES_M) x (BN/WAVES_N) block of C held in 32 x 32 accumulators of
-//    v_mfma_f32_32x32x2_f32.  Ragged edges are zero-filled on load and
-//    masked on store, so every shape runs on this path.
+//  * gemm_f32_mfma_dma<Tile, SK, SPLIT>: the main kernel.  One workgroup per
+//    BM x BN tile of C; K is walked in BK-deep panels that buffer loads write
+//    straight into a ring of LDS buffers, so later panels are fetched while
+//    the matrix cores work on the current one (one barrier per panel).  Each
+//    wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of C held in 32 x 32
+//    accumulators of v_mfma_f32_32x32x2_f32; optional K-split wave groups
+//    inside the workgroup, stream-K across workgroups (SK) and split-K
+//    through a caller's workspace (SPLIT).  Ragged edges are zero-filled on
+//    load and masked on store, so every shape runs on this path.
+//  * gemm_f32_mfma<Tile, VEC_A, VEC_B>: the same tiling with panels staged
+//    global -> VGPR -> LDS, for rows too long for 32-bit buffer offsets.
 //  * gemm_f32_valu: a 64 x 64 LDS-tiled vector-FMA kernel (4 x 4 outputs per
 //    thread) for problems too small to fill a matrix-core tile.
+//  * fill_zero (K = 0), zero_shared_tiles (stream-K) and splitk_reduce
+//    (split-K) as helpers.
 //
 // The pages' kernels (Lecture 5 and 12 notes, the cuda-gemm README) were
 // written for NVIDIA parts; what carries over is the structure -- output
@@ -123,7 +129,7 @@ __device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncol
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core kernel
+// Tile parameters, and the register-staged matrix-core kernel
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KSPLIT_ = 1, int STAGES_ = 2,
           int GROUP_ = 8, int LOADERS_ = 0>
