@@ -101,17 +101,28 @@ def time_gemm(torch, gb, M, N, K, steps, warmup, config=-1, min_warm_s=0.0):
     return out
 
 
+def code_digest(path):
+    """sha256 of a C++ source with its // comments and blank lines removed, so
+    that editing comments does not count as changing the kernels."""
+    lines = []
+    for line in open(path, encoding="utf-8"):
+        code = line.split("//", 1)[0].rstrip()
+        if code:
+            lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def measured_traffic(kernel_desc, M, N, K):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
     record for this kernel and shape, or None if there is none or the kernel
-    source has changed since the counters were taken."""
+    code has changed since the counters were taken."""
     src = os.path.join(ROOT, "dense_fp32_gemm_amd", "csrc", "gemm_f32.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    sha = code_digest(src)
     name = kernel_desc.split()[0]
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_traffic.json")):
         rec = json.load(open(path))
         if (rec.get("kernel") == name and rec.get("workload") == f"{M}x{N}x{K}"
-                and rec.get("source_sha256") == sha):
+                and rec.get("code_sha256") == sha):
             return int(round(rec["bytes_per_launch"]))
     return None
 
