@@ -1250,14 +1250,15 @@ using TileSplitK = Tile64x64K32S4;
 constexpr int kSplitKMinPanels = 8;     // 32-deep panels per slice, at least
 
 // Slices for this shape, or 1 when split-K does not apply: only while the
-// 64 x 64 tiles fill at most a quarter of the CUs, as many slices as fill
-// them, each at least kSplitKMinPanels panels deep.
+// 64 x 64 tiles fill at most half of the CUs, as many slices as fill them,
+// each at least kSplitKMinPanels panels deep (640 x 640 x 8192, 100 tiles:
+// 147 us without, 82 us with two slices).
 int splitk_slices(int M, int N, int K)
 {
     if (M < 16 || N < 16 || K <= 0)
         return 1;
     const int64_t t = ceil_div(M, TileSplitK::BM) * ceil_div(N, TileSplitK::BN);
-    if (4 * t > kComputeUnits)
+    if (2 * t > kComputeUnits)
         return 1;
     int64_t slices = kComputeUnits / t;
     const int64_t by_depth = ceil_div(K, TileSplitK::BK) / kSplitKMinPanels;

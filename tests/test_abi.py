@@ -202,8 +202,10 @@ def test_streamk_grid_is_one_worker_per_compute_unit():
 def test_split_k_workspace_size():
     # 200 x 200: 16 tiles of 64 x 64 -> 16 slices of a 20000-deep K
     assert gb.gemm_f32_ws_size(200, 200, 20000) == 16 * 200 * 200 * 4
-    # slices also limited by K: 625 panels of 32 -> at most 78 slices of 8 panels
+    # slices also limited by K: 32 panels of 32 -> at most 4 slices of 8 panels
     assert gb.gemm_f32_ws_size(64, 64, 1024) == 4 * 64 * 64 * 4
+    # 100 tiles fill up to 2 slices
+    assert gb.gemm_f32_ws_size(640, 640, 8192) == 2 * 640 * 640 * 4
     # enough tiles, too short a K, tiny or invalid shapes: not split
     for shape in [(8192, 8192, 8192), (2048, 2048, 2048), (1024, 1024, 8192), (64, 64, 256),
                   (200, 200, 0), (8, 8, 100000), (-1, 200, 20000)]:
