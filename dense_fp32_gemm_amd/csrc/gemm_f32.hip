@@ -908,7 +908,7 @@ enum ConfigId {
     kCfgDma128x128K32,
     kCfgDma64x64K32SK,
     kCfgDma128x128K32W16SK,
-    kCfgDma256x256W16SK,
+    kCfgDma256x256K32W16SK,
     kCfgDma64x64K64,
     kCfgDma64x64K64SK,
     kCfgDma128x128K32S2,
@@ -1046,7 +1046,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile128x128K32>("dma_128x128x32"),
     config_streamk<Tile64x64K32>("dma_64x64x32_sk"),
     config_streamk<Tile128x128K32W16>("dma_128x128x32_w16_sk"),
-    config_streamk<Tile256x256W16>("dma_256x256x16_w16_sk"),
+    config_streamk<Tile256x256K32W16>("dma_256x256x32_w16_sk"),
     config_dma<Tile64x64K64>("dma_64x64x64"),
     config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
     config_dma<Tile128x128K32S2>("dma_128x128x32_ksplit2"),
@@ -1115,7 +1115,7 @@ int select_config(int M, int N, int K, bool dma_ok)
     if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128;
     if (tiles(kCfgDma256x256K32W16) >= kComputeUnits)
-        return unbalanced(kCfgDma256x256K32W16) ? kCfgDma256x256W16SK : kCfgDma256x256K32W16;
+        return unbalanced(kCfgDma256x256K32W16) ? kCfgDma256x256K32W16SK : kCfgDma256x256K32W16;
     if (tiles(kCfgDma128x128K32W16) >= kComputeUnits) {
         if (!unbalanced(kCfgDma128x128K32W16))
             return kCfgDma128x128K32S2;

@@ -154,7 +154,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # 272, 400 and 400 tiles: the last round would leave most CUs idle
     ((1025, 1023, 1000), "dma_64x64x64_sk "), ((2560, 2560, 2560), "dma_128x128x32_w16_sk "),
-    ((5000, 5000, 5000), "dma_256x256x16_w16_sk "),
+    ((5000, 5000, 5000), "dma_256x256x32_w16_sk "),
     # 400 64 x 64 tiles: two rounds, resident together; 576: 32-deep panels
     ((1280, 1280, 1280), "dma_64x64x64 "), ((1536, 1536, 1536), "dma_64x64x32 "),
     # 289 128 x 128 tiles but K < 2048: 1122 64 x 64 tiles instead

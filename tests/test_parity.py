@@ -329,7 +329,7 @@ def test_random_shapes_layouts_and_configs(dev):
 STREAMK = [("dma_64x64x64_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
            ("dma_64x64x64_sk", (1100, 1050, 200)),
            ("dma_128x128x32_w16_sk", (2176, 2100, 1000)),
-           ("dma_256x256x16_w16_sk", (4352, 4200, 200))]
+           ("dma_256x256x32_w16_sk", (4352, 4200, 200))]
 
 
 @pytest.mark.parametrize("name,shape", STREAMK, ids=[f"{n}-{'x'.join(map(str, s))}" for n, s in STREAMK])
