@@ -218,3 +218,14 @@ def test_split_k_entry_point_validates_like_gemm_f32():
     assert gb.gemm_f32_ws(5, 9, 8, FAKE, 7, FAKE, 9, FAKE, 9, FAKE, ws, 0) == gb.GEMM_F32_ERR_LD
     assert gb.gemm_f32_ws(5, 9, 8, 0, 8, FAKE, 9, FAKE, 9, FAKE, ws, 0) == gb.GEMM_F32_ERR_NULL
     assert gb.gemm_f32_ws(0, 9, 8, 0, 8, 0, 9, 0, 9, 0, 0, 0) == gb.GEMM_F32_OK
+
+
+def test_traffic_records_key_on_code_not_comments(tmp_path):
+    import bench
+    a = tmp_path / "a.hip"
+    a.write_text("int f(int x)\n{\n    return x + 1;   // one more\n}\n")
+    b = tmp_path / "b.hip"
+    b.write_text("// a new comment line\nint f(int x)\n{\n\n    return x + 1;   // one more, said again\n}\n")
+    c = tmp_path / "c.hip"
+    c.write_text("int f(int x)\n{\n    return x + 2;\n}\n")
+    assert bench.code_digest(a) == bench.code_digest(b) != bench.code_digest(c)
