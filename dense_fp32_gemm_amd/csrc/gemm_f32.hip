@@ -132,7 +132,7 @@ __device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncol
 // Tile parameters, and the register-staged matrix-core kernel
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KSPLIT_ = 1, int STAGES_ = 2,
-          int GROUP_ = 8, int LOADERS_ = 0>
+          int GROUP_ = 8, int LOADERS_ = 0, int PIPE_ = 0>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -162,6 +162,9 @@ struct MfmaTile {
     // Waves of each group that issue the direct-to-LDS panel loads (the
     // lowest-numbered ones; 0: all of them).
     static constexpr int kLoaders = LOADERS_ ? LOADERS_ : WAVES_M * WAVES_N;
+    // Software-pipelined rounds (direct-to-LDS kernel, 4-wave tiles): see
+    // the pipelined branch of gemm_f32_mfma_dma.
+    static constexpr bool kPipe = PIPE_ != 0;
 
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
     static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
@@ -557,6 +560,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 for (int j = 0; j < FN; ++j)
                     f.b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
         };
+        // The instructions s0 .. s1-1 of a k-group (all 32 x 32 blocks).
+        auto mma_part = [&](const Frag &f, int s0, int s1) {
+#pragma unroll
+            for (int s = s0; s < s1; ++s)
+#pragma unroll
+                for (int i = 0; i < FM; ++i)
+#pragma unroll
+                    for (int j = 0; j < FN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[i][s], f.b[s][j], acc[i][j], 0, 0, 0);
+        };
         auto mma = [&](const Frag &f) {
 #pragma unroll
             for (int s = 0; s < 4; ++s)
@@ -594,6 +607,140 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     stage[buf][r * BK + 4 * (chunk ^ swz_a<BK>(r)) + x] = 0.f;
             }
         };
+        if constexpr (T::kPipe) {
+            // Software-pipelined rounds.  A 4-wave tile has one wave per
+            // SIMD, so no other wave fills the matrix core while this one
+            // waits: the wave's own instruction stream must keep it busy.
+            //  - Fragments are read one k-group ahead (two Frag sets), and
+            //    each read is issued between two MFMAs of the k-group before.
+            //  - The panel loads of round it+1 are spread through the MFMAs
+            //    of round it, one load every kGap MFMAs from the first
+            //    k-groups on, into the buffer round it-1 used.
+            //  - One barrier per round, halfway through the last k-group: the
+            //    wave's own loads have landed (vmcnt), all waves are done
+            //    with the buffer of round it (their last reads fed the MFMAs
+            //    before it), and the first fragments of round it+1 are read
+            //    while the second half of those MFMAs runs.
+            //  - Per round only scalars change.  The per-lane offsets are the
+            //    tile's (rows past M-1 and columns past N-1 read as zero);
+            //    in the last panel (k0 + BK > K) B's range ends after B's
+            //    last element, so its rows past K-1 read as zero, and A's
+            //    columns past K-1 are set to +0.0 in LDS once the panel has
+            //    landed (A's range also ends after A's last element when that
+            //    is within the panel's reach).  Past the last round the
+            //    ranges are empty and the loads only write zeros into the
+            //    idle buffer.
+            // The sched_group_barrier masks: 0x008 MFMA, 0x100 LDS read,
+            // 0x060 buffer load (a direct-to-LDS load counts as a load and
+            // a store).  Measured at 8192^3: 7.30 ms against 7.45 for the
+            // 16-wave 256 x 256 tile; 2048^3 with 128 x 128 x 64 tiles:
+            // 125 us against 132.6 for the 16-wave K-split tile.
+            constexpr int Q = BK / 8;                            // k-groups per panel
+            constexpr int kMfma = 4 * FM * FN;                   // MFMAs per k-group
+            constexpr int kReads = FM + 2 * FN;                  // LDS reads per k-group (B in pairs)
+            constexpr int kGap = 3;                              // MFMAs before each panel load
+            constexpr int kPerBlock = (kMfma - kReads) / kGap;   // panel loads per k-group
+            static_assert(KS == 1 && S == 2 && Q % 2 == 0 && NL == NW && kEvenA && kEvenB,
+                          "pipelined rounds: one group of all-loading waves, two buffers, even k-group count");
+            static_assert(kPerBlock >= 1 && (kLoads + kPerBlock - 1) / kPerBlock <= Q - 1,
+                          "the panel loads fit in the k-groups before the barrier");
+            uint32_t oa_t[kLoadsA], ob_t[kLoadsB];
+#pragma unroll
+            for (int j = 0; j < kLoadsA; ++j)
+                oa_t[j] = m0 + a_r[j] < g.M ? a_off[j] : kOutOfRange;
+#pragma unroll
+            for (int j = 0; j < kLoadsB; ++j)
+                ob_t[j] = n0 + b_c[j] < g.N ? b_off[j] : kOutOfRange;
+            struct Rsrc {
+                __amdgpu_buffer_rsrc_t a, b;
+            };
+            auto rsrc = [&](int k0, bool on) {
+                const bool last = k0 + BK > g.K;
+                const int64_t a_end = 4 * ((int64_t)(g.M - 1 - m0) * g.lda + (g.K - k0));
+                const int ar = !on ? 0 : (last && a_end < (int64_t)kOutOfRange) ? (int)a_end : (int)kOutOfRange;
+                const int br = !on ? 0 : last ? 4 * ((g.K - 1 - k0) * (int)g.ldb + (g.N - n0)) : (int)kOutOfRange;
+                return Rsrc{__builtin_amdgcn_make_buffer_rsrc((void *)(g.A + ((int64_t)m0 * g.lda + k0)), 0, ar,
+                                                              kRawBufferFlags),
+                            __builtin_amdgcn_make_buffer_rsrc((void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0, br,
+                                                              kRawBufferFlags)};
+            };
+            // Load x of a wave's panel share (A's loads first, then B's).
+            auto load_one = [&](int buf, const Rsrc &r, int x) {
+                if (x < kLoadsA)
+                    buffer_to_lds(r.a, &stage[buf][(lw * kLoadsA + x) * kSpanA], oa_t[x]);
+                else
+                    buffer_to_lds(r.b, &stage[buf][kA + (lw * kLoadsB + x - kLoadsA) * kSpanB], ob_t[x - kLoadsA]);
+            };
+            const bool cols_tail = g.K % BK != 0 && p_end == ktiles;
+            const int cols_round = ktiles - 1 - p_begin;
+            auto clear_cols = [&](int buf) {
+                const int valid = g.K - (ktiles - 1) * BK;
+                for (int e = tid; e < BM * BK; e += T::kThreads) {
+                    const int r = e / BK, c = e % BK;
+                    if (c >= valid)
+                        stage[buf][r * BK + 4 * ((c / 4) ^ swz_a<BK>(r)) + c % 4] = 0.f;
+                }
+            };
+            {
+                const Rsrc r0 = rsrc(panel_k(0), true);
+#pragma unroll
+                for (int x = 0; x < kLoads; ++x)
+                    load_one(0, r0, x);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+            if (cols_tail && cols_round == 0) {
+                clear_cols(0);
+                __syncthreads();
+            }
+            Frag F[2];
+            read_frag(F[0], 0, 0);
+            for (int it = 0; it < rounds; ++it) {
+                const int buf = it & 1;
+                const Rsrc nx = rsrc(panel_k(it + 1), it + 1 < rounds);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int q = 0; q + 1 < Q; ++q) {
+                    read_frag(F[(q + 1) & 1], buf, q + 1);
+#pragma unroll
+                    for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
+                        if (x < kLoads)
+                            load_one(buf ^ 1, nx, x);
+                    mma(F[q & 1]);
+#pragma unroll
+                    for (int r = 0; r < kReads; ++r) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+#pragma unroll
+                    for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
+                        if (x < kLoads) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, kGap, 0);
+                            __builtin_amdgcn_sched_group_barrier(0x060, 1, 0);
+                        }
+                    __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                mma_part(F[(Q - 1) & 1], 0, 2);
+                __builtin_amdgcn_sched_barrier(0);
+                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                __builtin_amdgcn_s_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                if (cols_tail && it + 1 == cols_round) {
+                    clear_cols(buf ^ 1);
+                    __syncthreads();
+                }
+                read_frag(F[0], buf ^ 1, 0);
+                mma_part(F[(Q - 1) & 1], 2, 4);
+#pragma unroll
+                for (int r = 0; r < kReads; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
         // Rounds it+1 .. it+S-1 are in flight while round it is computed.
 #pragma unroll
         for (int it = 0; it < S - 1; ++it)
@@ -626,6 +773,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     mma(f);
                 }
             }
+        }
         }
         // Every wave is done with the panel buffers before they are reused
         // (by the K-split reduction, or by the next tile's first loads).
@@ -885,6 +1033,9 @@ using Tile128x128K32 = MfmaTile<128, 128, 32, 2, 2>;
 using Tile64x64K64 = MfmaTile<64, 64, 64, 2, 2>;         // 64-deep panels
 // 2 K-split groups of 8 waves of 32 x 64, 4 of them loading
 using Tile128x128K32S2 = MfmaTile<128, 128, 32, 4, 2, 2, 2, 8, 4>;
+// Software-pipelined 4-wave tiles: 4 waves of 128 x 128, and of 64 x 64
+using Tile256x256K32P = MfmaTile<256, 256, 32, 2, 2, 1, 2, 8, 0, 1>;
+using Tile128x128K64P = MfmaTile<128, 128, 64, 2, 2, 1, 2, 8, 0, 1>;
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -912,6 +1063,10 @@ enum ConfigId {
     kCfgDma64x64K64,
     kCfgDma64x64K64SK,
     kCfgDma128x128K32S2,
+    kCfgDma256x256K32P,
+    kCfgDma256x256K32PSK,
+    kCfgDma128x128K64P,
+    kCfgDma128x128K64PSK,
     kNumConfigs
 };
 
@@ -1050,6 +1205,10 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile64x64K64>("dma_64x64x64"),
     config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
     config_dma<Tile128x128K32S2>("dma_128x128x32_ksplit2"),
+    config_dma<Tile256x256K32P>("dma_256x256x32_pipe"),
+    config_streamk<Tile256x256K32P>("dma_256x256x32_pipe_sk"),
+    config_dma<Tile128x128K64P>("dma_128x128x64_pipe"),
+    config_streamk<Tile128x128K64P>("dma_128x128x64_pipe_sk"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1066,18 +1225,19 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 }
 
 // Tile choice by shape, from the configuration sweep (sweep.py) on MI355X.
-// Output tiles are the unit of parallelism, and a compute unit needs several
-// waves per SIMD to keep its matrix cores fed, so the rule prefers big tiles
-// with 16 waves when there are enough of them (256 compute units):
+// Output tiles are the unit of parallelism; the rule prefers the biggest
+// tiles of which there are enough for the 256 compute units:
 //  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 4 waves
 //    (short K: per-tile start-up and the C store weigh more than reuse);
-//  * at least one 256 x 256 tile per CU: 256 x 256, 16 waves of 64 x 64,
-//    32-deep panels (+1.5 % over 16-deep at 4096^3 and 8192^3 on one box,
-//    equal on another);
-//  * at least one 128 x 128 tile per CU: 128 x 128, 16 waves in two K-split
-//    groups of 8 waves of 32 x 64 (+0.7 to +3.6 % over one group of 16
-//    waves of 32 x 32: 2048^3, 2048 x 2048 x 4096, 4096 x 2048 x 2048,
-//    1024 x 8192 x 8192);
+//  * at least one 256 x 256 tile per CU: 256 x 256 with 4 software-pipelined
+//    waves of 128 x 128, 32-deep panels (8192^3: 7.31 ms against 7.45 for
+//    16 waves of 64 x 64; 4096 x 4096 x 16384: 3.66 against 3.72);
+//  * at least one 128 x 128 tile per CU: 128 x 128 with 4 pipelined waves
+//    of 64 x 64, 64-deep panels (2048^3: 125 us against 133 for 16 waves in
+//    two K-split groups);
+//  * at least three quarters of the CUs busy with 128 x 128 tiles while
+//    64 x 64 tiles would leave the last round mostly idle: the pipelined
+//    128 x 128 tile too (1792^3: 110 us against 121 for 64 x 64);
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
 //    shapes): 64 x 64 with K split over four wave groups inside the
 //    workgroup, 16 waves instead of 4 on the CU (1024^3: 24.6 us against
@@ -1086,17 +1246,19 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    else 64 x 64.
 // When a tile count just above a multiple of 256 would leave most CUs idle
 // in the last round, a stream-K twin spreads all tiles' K-panels evenly over
-// one workgroup per CU (measured: 5000^3 1921 us against 2381 for 256 x 256
-// tiles; (1025, 1023, 1000) 36.8 us against 42.4 for 64 x 64); for 128 x 128
-// tiles only with K >= 2048 (2560^3: 282 us against 315), since below that
-// 64 x 64 tiles do better ((2176, 2100, 1000): 93 us against 108).
-// Below the two largest tiles the choices use 32- or 64-deep K-panels: those
+// one workgroup per CU (5000^3: 1832 us against 2381 for 256 x 256 tiles;
+// (1025, 1023, 1000) 36.8 us against 42.4 for 64 x 64); for 128 x 128 tiles
+// only with K >= 2048 (3072^3: 428 us against 455 for 64 x 64), since below
+// that 64 x 64 tiles do better ((2176, 2100, 1000): 92 us).
+// Below the largest tile the choices use 32- or 64-deep K-panels: those
 // tiles give each wave few MFMAs per panel, so fewer, deeper panels cut the
 // per-panel barrier, wait and LDS-latency cost (64-deep: +3 to +5 % at 1280^3
-// and 2048 x 1024 x 1024, one or two 64 x 64 tiles per CU).  Problems with
+// and 2048 x 1024 x 1024, one or two 64 x 64 tiles per CU).  With deep_ok
+// false (64-deep panels too tall for 32-bit offsets at the caller's leading
+// dimensions) the 32-deep alternatives are chosen instead.  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
-int select_config(int M, int N, int K, bool dma_ok)
+int select_config(int M, int N, int K, bool dma_ok, bool deep_ok)
 {
     if (M < 16 || N < 16)
         return kCfgValu64;
@@ -1114,15 +1276,20 @@ int select_config(int M, int N, int K, bool dma_ok)
     };
     if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128;
-    if (tiles(kCfgDma256x256K32W16) >= kComputeUnits)
-        return unbalanced(kCfgDma256x256K32W16) ? kCfgDma256x256K32W16SK : kCfgDma256x256K32W16;
-    if (tiles(kCfgDma128x128K32W16) >= kComputeUnits) {
-        if (!unbalanced(kCfgDma128x128K32W16))
-            return kCfgDma128x128K32S2;
+    if (tiles(kCfgDma256x256K32P) >= kComputeUnits)
+        return unbalanced(kCfgDma256x256K32P) ? kCfgDma256x256K32PSK : kCfgDma256x256K32P;
+    const int64_t t128 = tiles(kCfgDma128x128K64P);
+    if (t128 >= kComputeUnits) {
+        if (!unbalanced(kCfgDma128x128K64P))
+            return deep_ok ? kCfgDma128x128K64P : kCfgDma128x128K32S2;
         // Stream-K's extra launch and split-tile passes pay off over a long
         // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
-        return K >= 2048 ? kCfgDma128x128K32W16SK : kCfgDma64x64K32;
+        if (K >= 2048)
+            return deep_ok ? kCfgDma128x128K64PSK : kCfgDma128x128K32W16SK;
+        return kCfgDma64x64K32;
     }
+    if (deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits && unbalanced(kCfgDma64x64K32))
+        return kCfgDma128x128K64P;
     if (tiles(kCfgDma64x64K32) <= kComputeUnits && K > 512)
         return kCfgDma64x64K32S4;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
@@ -1137,8 +1304,10 @@ int select_config(int M, int N, int K, bool dma_ok)
     // not double the time.
     const int64_t t64 = tiles(kCfgDma64x64K64);
     if (t64 > kComputeUnits && 4 * t64 <= 5 * kComputeUnits)
-        return kCfgDma64x64K64SK;
-    return t64 <= 2 * kComputeUnits ? kCfgDma64x64K64 : kCfgDma64x64K32;
+        return deep_ok ? kCfgDma64x64K64SK : kCfgDma64x64K32SK;
+    if (t64 <= 2 * kComputeUnits)
+        return deep_ok ? kCfgDma64x64K64 : kCfgDma64x64K32;
+    return kCfgDma64x64K32;
 }
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
@@ -1177,11 +1346,14 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     }
     int c = config;
     if (c < 0) {
-        // The rule's direct-to-LDS choice, unless its panels are too tall or
-        // deep for 32-bit offsets at these leading dimensions.
-        c = select_config(M, N, K, true);
+        // The rule's direct-to-LDS choice; if its panels are too tall or deep
+        // for 32-bit offsets at these leading dimensions, its choice among
+        // 32-deep panels, and failing that the register-staged kernel.
+        c = select_config(M, N, K, true, true);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, false);
+            c = select_config(M, N, K, true, false);
+        if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
+            c = select_config(M, N, K, false, false);
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }

@@ -133,28 +133,34 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 4096, 4096, 1000, FAKE, 1000, FAKE, ldb, FAKE, 4096)
     assert text.startswith("staged"), text
     # 63 rows of B span more than 2 GiB but 31 do not: the rule's 64-deep
-    # choice for two 64 x 64 tiles per CU is replaced, a 32-deep one is kept
+    # choices give way to its 32-deep ones
     ldb = 10_000_000
     rc, text = gb.gemm_f32_describe(-1, 2048, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
-    assert rc == gb.GEMM_F32_OK and text.startswith("staged"), text
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32 "), text
     rc, text = gb.gemm_f32_describe(-1, 2048, 2048, 2048, FAKE, 2048, FAKE, ldb, FAKE, 2048)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_ksplit2 "), text
+    rc, text = gb.gemm_f32_describe(-1, 3072, 3072, 3072, FAKE, 3072, FAKE, ldb, FAKE, 3072)
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16_sk "), text
+    rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_sk "), text
     k64 = gb.config_names().index("dma_64x64x64")
     rc, _ = gb.gemm_f32_describe(k64, 1024, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
     assert rc == gb.GEMM_F32_ERR_CONFIG
 
 
 @pytest.mark.parametrize("shape,name", [
-    ((8192, 8192, 8192), "dma_256x256x32_w16 "), ((2048, 2048, 2048), "dma_128x128x32_ksplit2 "),
-    ((4096, 4096, 16384), "dma_256x256x32_w16 "), ((1024, 8192, 8192), "dma_128x128x32_ksplit2 "),
+    ((8192, 8192, 8192), "dma_256x256x32_pipe "), ((2048, 2048, 2048), "dma_128x128x64_pipe "),
+    ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x64_pipe "),
     ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
     ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
     ((1000, 1000, 1000), "dma_64x64x32_ksplit4"), ((512, 512, 1024), "dma_64x64x32_ksplit4"),
     ((512, 512, 512), "dma_64x64x64 "), ((2048, 1024, 1024), "dma_64x64x64 "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # 272, 400 and 400 tiles: the last round would leave most CUs idle
-    ((1025, 1023, 1000), "dma_64x64x64_sk "), ((2560, 2560, 2560), "dma_128x128x32_w16_sk "),
-    ((5000, 5000, 5000), "dma_256x256x32_w16_sk "),
+    ((1025, 1023, 1000), "dma_64x64x64_sk "), ((2560, 2560, 2560), "dma_128x128x64_pipe_sk "),
+    ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_sk "),
+    # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
+    ((1792, 1792, 1792), "dma_128x128x64_pipe "), ((3072, 1024, 2048), "dma_64x64x32 "),
     # 400 64 x 64 tiles: two rounds, resident together; 576: 32-deep panels
     ((1280, 1280, 1280), "dma_64x64x64 "), ((1536, 1536, 1536), "dma_64x64x32 "),
     # 289 128 x 128 tiles but K < 2048: 1122 64 x 64 tiles instead
