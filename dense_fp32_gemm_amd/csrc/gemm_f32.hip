@@ -370,7 +370,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int NW = T::kGroupWaves;                // waves per K-split group
     constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
-    static_assert(!SK || KS == 1, "stream-K splits K across workgroups, not inside one");
     static_assert(!(SK && SPLIT), "one way of splitting K across workgroups at a time");
     static_assert(BK == 16 || BK == 32 || BK == 64, "the A layout permutes the 16-byte chunks of 16-, 32- or 64-deep rows");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
@@ -608,9 +607,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             }
         };
         if constexpr (T::kPipe) {
-            // Software-pipelined rounds.  A 4-wave tile has one wave per
-            // SIMD, so no other wave fills the matrix core while this one
-            // waits: the wave's own instruction stream must keep it busy.
+            // Software-pipelined rounds, for 4-wave tiles and for K-split
+            // tiles of one-wave groups.  With one or two waves per SIMD,
+            // little else fills the matrix core while a wave waits: the
+            // wave's own instruction stream must keep it busy.
             //  - Fragments are read one k-group ahead (two Frag sets), and
             //    each read is issued between two MFMAs of the k-group before.
             //  - The panel loads of round it+1 are spread through the MFMAs
@@ -620,7 +620,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             //    wave's own loads have landed (vmcnt), all waves are done
             //    with the buffer of round it (their last reads fed the MFMAs
             //    before it), and the first fragments of round it+1 are read
-            //    while the second half of those MFMAs runs.
+            //    while the second half of those MFMAs runs.  A one-wave
+            //    group owns its buffers and only waits for its own loads.
+            //    (8 such groups on a 64 x 64 tile: 16384 x 64 x 4096 in 72 us
+            //    against 79 for 4 groups of 4 waves.)
             //  - Per round only scalars change.  The per-lane offsets are the
             //    tile's (rows past M-1 and columns past N-1 read as zero);
             //    in the last panel (k0 + BK > K) B's range ends after B's
@@ -638,10 +641,14 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             constexpr int Q = BK / 8;                            // k-groups per panel
             constexpr int kMfma = 4 * FM * FN;                   // MFMAs per k-group
             constexpr int kReads = FM + 2 * FN;                  // LDS reads per k-group (B in pairs)
-            constexpr int kGap = 3;                              // MFMAs before each panel load
+            // MFMAs before each panel load: 3 where the loads fit, fewer for
+            // small wave tiles, which have few MFMAs per load.
+            constexpr int kGapFit = (kMfma - kReads) * (Q - 1) / kLoads;
+            constexpr int kGap = kGapFit < 3 ? (kGapFit < 1 ? 1 : kGapFit) : 3;
             constexpr int kPerBlock = (kMfma - kReads) / kGap;   // panel loads per k-group
-            static_assert(KS == 1 && S == 2 && Q % 2 == 0 && NL == NW && kEvenA && kEvenB,
-                          "pipelined rounds: one group of all-loading waves, two buffers, even k-group count");
+            static_assert((KS == 1 || NW == 1) && S == 2 && Q % 2 == 0 && NL == NW && kEvenA && kEvenB,
+                          "pipelined rounds: one group of all-loading waves, or one-wave groups; two buffers; "
+                          "even k-group count");
             static_assert(kPerBlock >= 1 && (kLoads + kPerBlock - 1) / kPerBlock <= Q - 1,
                           "the panel loads fit in the k-groups before the barrier");
             uint32_t oa_t[kLoadsA], ob_t[kLoadsB];
@@ -671,16 +678,27 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 else
                     buffer_to_lds(r.b, &stage[buf][kA + (lw * kLoadsB + x - kLoadsA) * kSpanB], ob_t[x - kLoadsA]);
             };
-            const bool cols_tail = g.K % BK != 0 && p_end == ktiles;
-            const int cols_round = ktiles - 1 - p_begin;
+            // This group's rounds: panels p_begin + group, + KS, ... below
+            // p_end; the panel holding column K-1 is its round tail_round if
+            // the group is tail_group.
+            const int my_rounds = npanels > group ? (npanels - group + KS - 1) / KS : 0;
+            const bool cols_tail = g.K % BK != 0 && p_end == ktiles && group == tail_group;
+            constexpr int NT = NW * kWaveSize;                   // threads of the group
             auto clear_cols = [&](int buf) {
                 const int valid = g.K - (ktiles - 1) * BK;
-                for (int e = tid; e < BM * BK; e += T::kThreads) {
+                for (int e = tid - group * NT; e < BM * BK; e += NT) {
                     const int r = e / BK, c = e % BK;
                     if (c >= valid)
                         stage[buf][r * BK + 4 * ((c / 4) ^ swz_a<BK>(r)) + c % 4] = 0.f;
                 }
             };
+            // A one-wave group needs no barrier: its LDS reads and writes are
+            // in program order, and vmcnt covers its own loads.
+            auto group_sync = [&]() {
+                if constexpr (NW > 1)
+                    __syncthreads();
+            };
+            if (my_rounds > 0) {
             {
                 const Rsrc r0 = rsrc(panel_k(0), true);
 #pragma unroll
@@ -688,16 +706,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     load_one(0, r0, x);
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
-            if (cols_tail && cols_round == 0) {
+            if constexpr (NW > 1)
+                __builtin_amdgcn_s_barrier();
+            if (cols_tail && tail_round == 0) {
                 clear_cols(0);
-                __syncthreads();
+                group_sync();
             }
             Frag F[2];
             read_frag(F[0], 0, 0);
-            for (int it = 0; it < rounds; ++it) {
+            for (int it = 0; it < my_rounds; ++it) {
                 const int buf = it & 1;
-                const Rsrc nx = rsrc(panel_k(it + 1), it + 1 < rounds);
+                const Rsrc nx = rsrc(panel_k(it + 1), it + 1 < my_rounds);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int q = 0; q + 1 < Q; ++q) {
@@ -724,11 +743,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 mma_part(F[(Q - 1) & 1], 0, 2);
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-                __builtin_amdgcn_s_barrier();
+                if constexpr (NW > 1)
+                    __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
-                if (cols_tail && it + 1 == cols_round) {
+                if (cols_tail && it + 1 == tail_round) {
                     clear_cols(buf ^ 1);
-                    __syncthreads();
+                    group_sync();
                 }
                 read_frag(F[0], buf ^ 1, 0);
                 mma_part(F[(Q - 1) & 1], 2, 4);
@@ -739,6 +759,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
                 __builtin_amdgcn_sched_barrier(0);
+            }
             }
         } else {
         // Rounds it+1 .. it+S-1 are in flight while round it is computed.
@@ -1036,6 +1057,9 @@ using Tile128x128K32S2 = MfmaTile<128, 128, 32, 4, 2, 2, 2, 8, 4>;
 // Software-pipelined 4-wave tiles: 4 waves of 128 x 128, and of 64 x 64
 using Tile256x256K32P = MfmaTile<256, 256, 32, 2, 2, 1, 2, 8, 0, 1>;
 using Tile128x128K64P = MfmaTile<128, 128, 64, 2, 2, 1, 2, 8, 0, 1>;
+// Software-pipelined K-split: 8 one-wave groups, each with the whole 64 x 64
+// tile for every 8th 16-deep panel
+using Tile64x64K16S8P = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
 
 enum ConfigId {
     kCfgValu64 = 0,
@@ -1067,6 +1091,9 @@ enum ConfigId {
     kCfgDma256x256K32PSK,
     kCfgDma128x128K64P,
     kCfgDma128x128K64PSK,
+    kCfgDma64x64K16S8P,
+    kCfgDma64x64K16S8PSK,
+    kCfgDma64x64K32S4SK,
     kNumConfigs
 };
 
@@ -1209,6 +1236,9 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_streamk<Tile256x256K32P>("dma_256x256x32_pipe_sk"),
     config_dma<Tile128x128K64P>("dma_128x128x64_pipe"),
     config_streamk<Tile128x128K64P>("dma_128x128x64_pipe_sk"),
+    config_dma<Tile64x64K16S8P>("dma_64x64x16_ksplit8_pipe"),
+    config_streamk<Tile64x64K16S8P>("dma_64x64x16_ksplit8_pipe_sk"),
+    config_streamk<Tile64x64K32S4>("dma_64x64x32_ksplit4_sk"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1239,15 +1269,22 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    64 x 64 tiles would leave the last round mostly idle: the pipelined
 //    128 x 128 tile too (1792^3: 110 us against 121 for 64 x 64);
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
-//    shapes): 64 x 64 with K split over four wave groups inside the
-//    workgroup, 16 waves instead of 4 on the CU (1024^3: 24.6 us against
-//    26.1 for 64-deep panels; 16384 x 64 x 4096: 77 us against 90);
+//    shapes): 64 x 64 with K split over wave groups inside the workgroup.
+//    For K >= 2048, 8 software-pipelined one-wave groups (16384 x 64 x 4096:
+//    72 us against 79 for 4 groups of 4 waves; 1024 x 1024 x 8192: 130
+//    against 149), below that 4 groups of 4 waves (1024^3: 25.4 us against
+//    26.3 for the 8 groups and 26.7 for 4 waves on 64-deep panels);
+//  * up to three rounds of 64 x 64 tiles with K > 512 and a last round under
+//    80 % full: stream-K over the 4-group K-split tile (1200 x 1200 x 4096:
+//    120 us against 149 for 64 x 64; 1536^3: 81 against 83); two balanced
+//    rounds with K >= 2048: the 8 pipelined groups (1300 x 1300 x 4096: 136
+//    us against 149);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // When a tile count just above a multiple of 256 would leave most CUs idle
 // in the last round, a stream-K twin spreads all tiles' K-panels evenly over
 // one workgroup per CU (5000^3: 1832 us against 2381 for 256 x 256 tiles;
-// (1025, 1023, 1000) 36.8 us against 42.4 for 64 x 64); for 128 x 128 tiles
+// (1025, 1023, 1000) 37.2 us against 42.3 for 64 x 64); for 128 x 128 tiles
 // only with K >= 2048 (3072^3: 428 us against 455 for 64 x 64), since below
 // that 64 x 64 tiles do better ((2176, 2100, 1000): 92 us).
 // Below the largest tile the choices use 32- or 64-deep K-panels: those
@@ -1290,8 +1327,18 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok)
     }
     if (deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits && unbalanced(kCfgDma64x64K32))
         return kCfgDma128x128K64P;
-    if (tiles(kCfgDma64x64K32) <= kComputeUnits && K > 512)
-        return kCfgDma64x64K32S4;
+    // 64 x 64 tiles with K > 512, up to three rounds of them: K split
+    // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
+    // for K >= 2048, else 4 groups of 4 waves; two balanced rounds with
+    // K >= 2048: the 8 pipelined groups; a last round under 80 % full:
+    // stream-K over the 4-group tile.
+    const int64_t t32 = tiles(kCfgDma64x64K32);
+    if (K > 512 && t32 <= kComputeUnits)
+        return K >= 2048 ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4;
+    if (K > 512 && t32 <= 3 * kComputeUnits && unbalanced(kCfgDma64x64K32))
+        return kCfgDma64x64K32S4SK;
+    if (K >= 2048 && t32 <= 2 * kComputeUnits)
+        return kCfgDma64x64K16S8P;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * kComputeUnits)
         return wide;

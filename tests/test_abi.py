@@ -142,6 +142,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 3072, 3072, 3072, FAKE, 3072, FAKE, ldb, FAKE, 3072)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16_sk "), text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4_sk "), text
+    rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 500, FAKE, 500, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_sk "), text
     k64 = gb.config_names().index("dma_64x64x64")
     rc, _ = gb.gemm_f32_describe(k64, 1024, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
@@ -151,23 +153,29 @@ def test_wide_rows_fall_back_to_staged_kernels():
 @pytest.mark.parametrize("shape,name", [
     ((8192, 8192, 8192), "dma_256x256x32_pipe "), ((2048, 2048, 2048), "dma_128x128x64_pipe "),
     ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x64_pipe "),
-    ((8192, 8192, 128), "dma_128x128x16 "), ((16384, 64, 4096), "dma_64x64x32_ksplit4"),
-    ((64, 16384, 4096), "dma_64x64x32_ksplit4"),
-    ((1000, 1000, 1000), "dma_64x64x32_ksplit4"), ((512, 512, 1024), "dma_64x64x32_ksplit4"),
-    ((512, 512, 512), "dma_64x64x64 "), ((2048, 1024, 1024), "dma_64x64x64 "),
+    ((8192, 8192, 128), "dma_128x128x16 "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
-    # 272, 400 and 400 tiles: the last round would leave most CUs idle
-    ((1025, 1023, 1000), "dma_64x64x64_sk "), ((2560, 2560, 2560), "dma_128x128x64_pipe_sk "),
-    ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_sk "),
+    # at most one 64 x 64 tile per CU: K split inside the workgroup, 8
+    # pipelined one-wave groups from K = 2048 on
+    ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 16384, 4096), "dma_64x64x16_ksplit8_pipe "),
+    ((1024, 1024, 8192), "dma_64x64x16_ksplit8_pipe "), ((100, 5000, 3000), "dma_64x64x16_ksplit8_pipe "),
+    ((1000, 1000, 1000), "dma_64x64x32_ksplit4 "), ((512, 512, 1024), "dma_64x64x32_ksplit4 "),
+    # K <= 512: no K split
+    ((512, 512, 512), "dma_64x64x64 "), ((1000, 1000, 300), "dma_64x64x64 "),
+    # 272, 289, 400 and 576 64 x 64 tiles: the last round would leave many
+    # CUs idle; stream-K over the K-split tile
+    ((1025, 1023, 1000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
+    ((1280, 1280, 1280), "dma_64x64x32_ksplit4_sk "), ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "),
+    ((1025, 1023, 300), "dma_64x64x64_sk "),
+    # two balanced rounds: the pipelined K split for K >= 2048, else 64 x 64
+    ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe "), ((2048, 1024, 1024), "dma_64x64x64 "),
+    # three rounds and more: 4-wave 64 x 64 tiles, several per CU
+    ((3072, 1024, 2048), "dma_64x64x32 "), ((2176, 2100, 1000), "dma_64x64x32 "),
+    # 400, 576 and 576 128 x 128 tiles, K >= 2048: stream-K over them
+    ((2560, 2560, 2560), "dma_128x128x64_pipe_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_sk "),
+    ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
-    ((1792, 1792, 1792), "dma_128x128x64_pipe "), ((3072, 1024, 2048), "dma_64x64x32 "),
-    # 400 64 x 64 tiles: two rounds, resident together; 576: 32-deep panels
-    ((1280, 1280, 1280), "dma_64x64x64 "), ((1536, 1536, 1536), "dma_64x64x32 "),
-    # 289 128 x 128 tiles but K < 2048: 1122 64 x 64 tiles instead
-    ((2176, 2100, 1000), "dma_64x64x32 "),
-    # long K: the in-workgroup K-split only while there is one tile per CU
-    ((1024, 1024, 8192), "dma_64x64x32_ksplit4"), ((1025, 1025, 4096), "dma_64x64x64_sk "),
-    ((1300, 1300, 4096), "dma_64x64x64 "),
+    ((1792, 1792, 1792), "dma_128x128x64_pipe "),
 ])
 def test_selection(shape, name):
     M, N, K = shape

@@ -326,10 +326,11 @@ def test_random_shapes_layouts_and_configs(dev):
 # Stream-K: more tiles than compute units, so the K-panels of some tiles are
 # split between two workgroups that add their partial sums into C.
 # ---------------------------------------------------------------------------
-STREAMK = [("dma_64x64x64_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
-           ("dma_64x64x64_sk", (1100, 1050, 200)),
-           ("dma_128x128x32_w16_sk", (2176, 2100, 1000)),
-           ("dma_256x256x32_w16_sk", (4352, 4200, 200))]
+STREAMK = [("dma_64x64x32_ksplit4_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
+           ("dma_64x64x16_ksplit8_pipe_sk", (1100, 1050, 2051)), ("dma_64x64x64_sk", (1100, 1050, 200)),
+           ("dma_64x64x64_sk", (1025, 1023, 1000)),
+           ("dma_128x128x32_w16_sk", (2176, 2100, 1000)), ("dma_128x128x64_pipe_sk", (2176, 2100, 1003)),
+           ("dma_256x256x32_w16_sk", (4352, 4200, 200)), ("dma_256x256x32_pipe_sk", (4352, 4200, 203))]
 
 
 @pytest.mark.parametrize("name,shape", STREAMK, ids=[f"{n}-{'x'.join(map(str, s))}" for n, s in STREAMK])
@@ -345,7 +346,7 @@ def test_streamk_bit_exact_and_padding_kept(dev, name, shape):
     assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 5):]).all()
 
 
-@pytest.mark.parametrize("name,shape", STREAMK[:3], ids=[f"{n}-{'x'.join(map(str, s))}" for n, s in STREAMK[:3]])
+@pytest.mark.parametrize("name,shape", STREAMK[:4], ids=[f"{n}-{'x'.join(map(str, s))}" for n, s in STREAMK[:4]])
 def test_streamk_uniform_within_tolerance_and_deterministic(dev, name, shape):
     """Each shared tile receives exactly two partial sums added to +0.0, and
     binary32 addition is commutative, so the result does not depend on which
@@ -386,7 +387,7 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
     dB = torch.from_numpy(B).to(dev)
     rc, desc = gb.gemm_f32_describe(-1, 1025, 1023, 1000, dA.data_ptr(), 1000, dB.data_ptr(), 1023,
                                     dA.data_ptr(), 1023)
-    assert desc.startswith("dma_64x64x64_sk "), desc
+    assert desc.startswith("dma_64x64x32_ksplit4_sk "), desc
     say("stream-K eager, graph and concurrent streams, 1025x1023x1000")
     eager = gb.matmul(dA, dB)
     torch.cuda.synchronize()
