@@ -1275,10 +1275,11 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    against 149), below that 4 groups of 4 waves (1024^3: 25.4 us against
 //    26.3 for the 8 groups and 26.7 for 4 waves on 64-deep panels);
 //  * up to three rounds of 64 x 64 tiles with K > 512 and a last round under
-//    80 % full: stream-K over the 4-group K-split tile (1200 x 1200 x 4096:
-//    120 us against 149 for 64 x 64; 1536^3: 81 against 83); two balanced
-//    rounds with K >= 2048: the 8 pipelined groups (1300 x 1300 x 4096: 136
-//    us against 149);
+//    half full: stream-K over the 4-group K-split tile (1200 x 1200 x 4096:
+//    120 us against 149 for 64 x 64; 1536^3: 81 against 83; but 1280^3, a
+//    last round 56 % full: 53 against 51 for 64 x 64); otherwise two rounds
+//    with K >= 2048: the 8 pipelined groups (1300 x 1300 x 4096: 136 us
+//    against 149);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // When a tile count just above a multiple of 256 would leave most CUs idle
@@ -1329,13 +1330,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok)
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them: K split
     // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
-    // for K >= 2048, else 4 groups of 4 waves; two balanced rounds with
-    // K >= 2048: the 8 pipelined groups; a last round under 80 % full:
-    // stream-K over the 4-group tile.
+    // for K >= 2048, else 4 groups of 4 waves; a last round under half full:
+    // stream-K over the 4-group tile; two rounds otherwise, with K >= 2048:
+    // the 8 pipelined groups.
     const int64_t t32 = tiles(kCfgDma64x64K32);
     if (K > 512 && t32 <= kComputeUnits)
         return K >= 2048 ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4;
-    if (K > 512 && t32 <= 3 * kComputeUnits && unbalanced(kCfgDma64x64K32))
+    const int64_t last = t32 - (ceil_div(t32, kComputeUnits) - 1) * kComputeUnits;   // tiles in the last round
+    if (K > 512 && t32 <= 3 * kComputeUnits && 2 * last < kComputeUnits)
         return kCfgDma64x64K32S4SK;
     if (K >= 2048 && t32 <= 2 * kComputeUnits)
         return kCfgDma64x64K16S8P;

@@ -162,10 +162,10 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1000, 1000, 1000), "dma_64x64x32_ksplit4 "), ((512, 512, 1024), "dma_64x64x32_ksplit4 "),
     # K <= 512: no K split
     ((512, 512, 512), "dma_64x64x64 "), ((1000, 1000, 300), "dma_64x64x64 "),
-    # 272, 289, 400 and 576 64 x 64 tiles: the last round would leave many
-    # CUs idle; stream-K over the K-split tile
+    # 272, 289 and 576 64 x 64 tiles: the last round would be under half
+    # full; stream-K over the K-split tile.  400 tiles: 64 x 64 tiles
     ((1025, 1023, 1000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
-    ((1280, 1280, 1280), "dma_64x64x32_ksplit4_sk "), ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "),
+    ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "), ((1280, 1280, 1280), "dma_64x64x64 "),
     ((1025, 1023, 300), "dma_64x64x64_sk "),
     # two balanced rounds: the pipelined K split for K >= 2048, else 64 x 64
     ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe "), ((2048, 1024, 1024), "dma_64x64x64 "),
