@@ -12,8 +12,11 @@
 //    wave owns a (BM/WAVES_M) x (BN/WAVES_N) block of C held in 32 x 32
 //    accumulators of v_mfma_f32_32x32x2_f32; optional K-split wave groups
 //    inside the workgroup, stream-K across workgroups (SK) and split-K
-//    through a caller's workspace (SPLIT).  Ragged edges are zero-filled on
-//    load and masked on store, so every shape runs on this path.
+//    through a caller's workspace (SPLIT).  The largest tiles (4 waves of
+//    128 x 128 or 64 x 64) and the K-split tile of one-wave groups run a
+//    software-pipelined round loop (PIPE) that interleaves fragment reads
+//    and panel loads with the MFMAs.  Ragged edges are zero-filled on load
+//    and masked on store, so every shape runs on this path.
 //  * gemm_f32_mfma<Tile, VEC_A, VEC_B>: the same tiling with panels staged
 //    global -> VGPR -> LDS, for rows too long for 32-bit buffer offsets.
 //  * gemm_f32_valu: a 64 x 64 LDS-tiled vector-FMA kernel (4 x 4 outputs per
