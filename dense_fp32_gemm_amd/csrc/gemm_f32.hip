@@ -33,6 +33,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <type_traits>
 #include <stdio.h>
 #include <string.h>
 
@@ -56,7 +57,15 @@ struct GemmArgs {
     int tiles_m, tiles_n;
     int slices;          // K slices of a split-K launch (1 otherwise)
     int64_t slab;        // floats between two slices' partial products in C
+    int strip_rows;      // rows M - strip_rows .. M-1 lie below the tile grid
+                         // (tiles_m * BM = M - strip_rows): the last tile
+                         // row's workgroups compute them with FMAs
 };
+
+// Most rows a remainder strip may hold, and its largest K: the strip's rows
+// of A are staged in LDS next to the partial sums.
+constexpr int kMaxStripRows = 4;
+constexpr int kMaxStripK = 2048;
 
 // ---------------------------------------------------------------------------
 // Tile scheduling
@@ -173,6 +182,23 @@ struct MfmaTile {
     static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
     static_assert(kLoaders >= 1 && kLoaders <= WAVES_M * WAVES_N, "loader waves");
 };
+
+// The tile that also computes remainder strips (64 x 64, 32-deep panels, 4
+// K-split groups of 4 waves): the only one the shape rule pairs with a
+// strip.  The strip code lives in a separate instantiation of its kernel
+// (STRIP), so the plain one keeps its registers (60 VGPRs against 83).
+using StripTile = MfmaTile<64, 64, 32, 2, 2, 4>;
+
+// Whether a direct-to-LDS tile's panel buffers hold a strip's partial sums
+// and A rows.
+template <class T>
+constexpr bool strip_fits()
+{
+    constexpr int stage = T::BM * T::BK + T::BK * T::BN;
+    constexpr int red = T::kThreads / T::BN * kMaxStripRows * T::BN;
+    return T::kThreads % T::BN == 0 && red + kMaxStripRows * kMaxStripK <= T::kSplit * T::kStages * stage;
+}
+static_assert(strip_fits<StripTile>(), "strip space in the strip tile's panel buffers");
 
 // One v_mfma_f32_32x32x2_f32 adds, for the 32 x 32 block it accumulates,
 // sum over t in {0,1} of a(i,t) * b(t,j), where lane l supplies a(l%32, l/32)
@@ -366,7 +392,7 @@ __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_bas
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, offset, 0, 0, 0);
 }
 
-template <class T, bool SK = false, bool SPLIT = false>
+template <class T, bool SK = false, bool SPLIT = false, bool STRIP = false>
 __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -374,6 +400,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     constexpr int KS = T::kSplit;
     constexpr int FM = T::kFragM, FN = T::kFragN;
     static_assert(!(SK && SPLIT), "one way of splitting K across workgroups at a time");
+    static_assert(!STRIP || (std::is_same<T, StripTile>::value && !SK && !SPLIT),
+                  "remainder strips: data-parallel launches of the strip tile");
     static_assert(BK == 16 || BK == 32 || BK == 64, "the A layout permutes the 16-byte chunks of 16-, 32- or 64-deep rows");
     static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
     constexpr int kA = BM * BK;                       // floats per A panel
@@ -892,6 +920,74 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 }
             }
         }
+
+        // Remainder strip (data-parallel launches only): the workgroups of
+        // the last tile row also compute rows M-strip_rows .. M-1 of their
+        // columns with vector FMAs.  The strip's rows of A are first copied
+        // to LDS (read there as broadcasts).  The lanes of a wave take
+        // consecutive columns and the waves contiguous K slices; each lane
+        // sums its slice in k order, loading B 8 rows at a time, then the
+        // slices' sums are added in slice order through LDS, so the result
+        // does not depend on scheduling.
+        if constexpr (STRIP)
+        if (g.strip_rows > 0 && tm == g.tiles_m - 1) {
+            constexpr int kSlices = T::kThreads / BN;
+            constexpr int kRed = kSlices * kMaxStripRows * BN;          // floats of partial sums
+            const int j = tid % BN, sl = tid / BN;
+            const int col = n0 + j;
+            const int r0 = g.M - g.strip_rows;
+            const int per = (g.K + kSlices - 1) / kSlices;
+            const int kb = sl * per, ke = min(g.K, kb + per);
+            float *red = &lds[0][0][0];
+            float *sa = red + kRed;                  // strip_rows x K floats of A
+            __syncthreads();
+            for (int e = tid; e < g.strip_rows * g.K; e += T::kThreads)
+                sa[e] = g.A[(int64_t)(r0 + e / g.K) * g.lda + e % g.K];
+            __syncthreads();
+            float part[kMaxStripRows] = {};
+            auto strip_sum = [&](auto rows) {
+                constexpr int R = decltype(rows)::value;
+                int k = kb;
+                for (; k + 8 <= ke; k += 8) {
+                    float bv[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        bv[u] = g.B[(int64_t)(k + u) * g.ldb + col];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            part[r] = fmaf(sa[r * g.K + k + u], bv[u], part[r]);
+                }
+                for (; k < ke; ++k) {
+                    const float bv = g.B[(int64_t)k * g.ldb + col];
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        part[r] = fmaf(sa[r * g.K + k], bv, part[r]);
+                }
+            };
+            if (col < g.N) {
+                switch (g.strip_rows) {
+                case 1: strip_sum(std::integral_constant<int, 1>()); break;
+                case 2: strip_sum(std::integral_constant<int, 2>()); break;
+                case 3: strip_sum(std::integral_constant<int, 3>()); break;
+                default: strip_sum(std::integral_constant<int, 4>()); break;
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kMaxStripRows; ++r)
+                red[(sl * kMaxStripRows + r) * BN + j] = part[r];
+            __syncthreads();
+            if (sl == 0 && col < g.N) {
+                for (int r = 0; r < g.strip_rows; ++r) {
+                    float sum = red[r * BN + j];
+                    for (int s2 = 1; s2 < kSlices; ++s2)
+                        sum += red[(s2 * kMaxStripRows + r) * BN + j];
+                    store_c(&cbase[(int64_t)(r0 + r) * g.ldc + col], sum);
+                }
+            }
+            __syncthreads();
+        }
     };
 
     if (SPLIT) {
@@ -1133,17 +1229,17 @@ struct PlainKernel {
 // The direct-to-LDS kernel has one instance per tile and mode: it loads 16
 // bytes per lane from any 4-byte aligned operand, so the load-width flags
 // of the plan do not apply to it.
-template <class T, bool SK = false, bool SPLIT = false>
+template <class T, bool SK = false, bool SPLIT = false, bool STRIP = false>
 struct LaunchDma {
     static hipError_t run(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
     {
-        hipLaunchKernelGGL((gemm_f32_mfma_dma<T, SK, SPLIT>), dim3(grid), dim3(T::kThreads), 0, s, g);
+        hipLaunchKernelGGL((gemm_f32_mfma_dma<T, SK, SPLIT, STRIP>), dim3(grid), dim3(T::kThreads), 0, s, g);
         return hipGetLastError();
     }
     static int occupancy()
     {
         int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_f32_mfma_dma<T, SK, SPLIT>, T::kThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_f32_mfma_dma<T, SK, SPLIT, STRIP>, T::kThreads, 0) !=
             hipSuccess)
             return -1;
         return n;
@@ -1299,8 +1395,9 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 // dimensions) the 32-deep alternatives are chosen instead.  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
-int select_config(int M, int N, int K, bool dma_ok, bool deep_ok)
+int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip)
 {
+    strip = 0;
     if (M < 16 || N < 16)
         return kCfgValu64;
     auto tiles = [&](int c) { return ceil_div(M, kConfigs[c].bm) * ceil_div(N, kConfigs[c].bn); };
@@ -1337,6 +1434,21 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok)
     // stream-K over the 4-group tile; two rounds otherwise, with K >= 2048:
     // the 8 pipelined groups.
     const int64_t t32 = tiles(kCfgDma64x64K32);
+    // A last tile row of at most kMaxStripRows rows that alone takes the
+    // tiles past one round: those rows become a strip computed with FMAs by
+    // the last full tile row, and the rest runs as one round of 4-group
+    // K-split tiles.  The strip's cost grows with rows x K (each of a
+    // workgroup's 16 waves reads K/16 rows of 64 B columns and does rows
+    // FMAs per k), so only up to 4096 (1025 x 1023 x 1000: 29.6 us against
+    // 37.3 for stream-K; 1026 x 1001 x 1001: 31.8 against 37.5; at 4 x 1500
+    // both take 44.8, at 3 x 2048 the strip is 10 % slower).
+    const int64_t t_full = (M / 64) * ceil_div(N, 64);
+    static_assert(std::is_same<Tile64x64K32S4, StripTile>::value, "the strip tile is the 4-group K-split tile");
+    if (K > 512 && K < kMaxStripK && M % 64 != 0 && (M % 64) * K <= 4096 && t_full <= kComputeUnits &&
+        t32 > kComputeUnits) {
+        strip = M % 64;
+        return kCfgDma64x64K32S4;
+    }
     if (K > 512 && t32 <= kComputeUnits)
         return K >= 2048 ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4;
     const int64_t last = t32 - (ceil_div(t32, kComputeUnits) - 1) * kComputeUnits;   // tiles in the last round
@@ -1369,6 +1481,7 @@ struct Plan {
     bool vec_a, vec_b;
     int tiles_m, tiles_n;
     int grid;
+    int strip_rows;      // rows below the tile grid, computed as a strip
 };
 
 // Validates the arguments (sizes, leading dimensions, configuration index,
@@ -1386,6 +1499,7 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     plan->config = -1;
     plan->vec_a = plan->vec_b = false;
     plan->tiles_m = plan->tiles_n = plan->grid = 0;
+    plan->strip_rows = 0;
     if (M == 0 || N == 0)
         return GEMM_F32_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr)))
@@ -1397,23 +1511,25 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
         return GEMM_F32_OK;
     }
     int c = config;
+    int strip = 0;
     if (c < 0) {
         // The rule's direct-to-LDS choice; if its panels are too tall or deep
         // for 32-bit offsets at these leading dimensions, its choice among
         // 32-deep panels, and failing that the register-staged kernel.
-        c = select_config(M, N, K, true, true);
+        c = select_config(M, N, K, true, true, strip);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, true, false);
+            c = select_config(M, N, K, true, false, strip);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, false, false);
+            c = select_config(M, N, K, false, false, strip);
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
-    const int64_t tm = ceil_div(M, kConfigs[c].bm);
+    const int64_t tm = strip ? (M - strip) / kConfigs[c].bm : ceil_div(M, kConfigs[c].bm);
     const int64_t tn = ceil_div(N, kConfigs[c].bn);
     if (tm * tn > INT32_MAX)
         return GEMM_F32_ERR_DIM;
     plan->config = c;
+    plan->strip_rows = strip;
     plan->tiles_m = (int)tm;
     plan->tiles_n = (int)tn;
     if (kConfigs[c].streamk)
@@ -1462,7 +1578,12 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     g.tiles_n = p.tiles_n;
     g.slices = 1;
     g.slab = 0;
-    const hipError_t err = kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
+    g.strip_rows = p.strip_rows;
+    // A plan with a remainder strip runs the strip tile's strip kernel (the
+    // rule pairs strips with that tile only).
+    const hipError_t err = p.strip_rows > 0
+                               ? LaunchDma<StripTile, false, false, true>::run(g, true, true, p.grid, stream)
+                               : kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
@@ -1524,6 +1645,7 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     g.tiles_n = (int)ceil_div(N, TileSplitK::BN);
     g.slices = slices;
     g.slab = (int64_t)M * N;
+    g.strip_rows = 0;
     const int grid = g.tiles_m * g.tiles_n * slices;
     hipError_t err = LaunchDma<TileSplitK, false, true>::run(g, true, true, grid, stream);
     if (err != hipSuccess)
@@ -1615,10 +1737,13 @@ int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
         snprintf(buf, (size_t)buflen, "invalid: %s", gemm_f32_status_string(rc));
     else if (p.config < 0)
         snprintf(buf, (size_t)buflen, "%s", p.grid ? "fill_zero" : "none");
-    else
-        snprintf(buf, (size_t)buflen, "%s tiles=%dx%d grid=%d threads=%d load_a=%s load_b=%s",
-                 kConfigs[p.config].name, p.tiles_m, p.tiles_n, p.grid,
-                 kConfigs[p.config].threads, p.vec_a ? "x4" : "x1", p.vec_b ? "x4" : "x1");
+    else {
+        const int n = snprintf(buf, (size_t)buflen, "%s tiles=%dx%d grid=%d threads=%d load_a=%s load_b=%s",
+                               kConfigs[p.config].name, p.tiles_m, p.tiles_n, p.grid,
+                               kConfigs[p.config].threads, p.vec_a ? "x4" : "x1", p.vec_b ? "x4" : "x1");
+        if (p.strip_rows > 0 && n >= 0 && n < buflen)
+            snprintf(buf + n, (size_t)(buflen - n), " strip_rows=%d", p.strip_rows);
+    }
     return rc;
 }
 

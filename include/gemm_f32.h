@@ -147,9 +147,10 @@ GEMM_F32_API int gemm_f32_config_info(int config, int *bm, int *bn, int *bk,
  * description of what gemm_f32_with_config(config, ...) would enqueue for
  * these arguments (config -1: what gemm_f32() would enqueue): the
  * configuration name first ("none" for an empty output, "fill_zero" for
- * K == 0), then tile grid, workgroup count and load widths.  Pointers are only
- * inspected for alignment, never dereferenced.  Returns the status the call
- * would return for the same arguments.
+ * K == 0), then tile grid, workgroup count and load widths, and, when the
+ * last 1-4 rows are computed as a strip below the tile grid, " strip_rows=R".
+ * Pointers are only inspected for alignment, never dereferenced.  Returns the
+ * status the call would return for the same arguments.
  */
 GEMM_F32_API int gemm_f32_describe(int config, int M, int N, int K,
                                    const float *A, int lda,

@@ -141,8 +141,10 @@ def test_wide_rows_fall_back_to_staged_kernels():
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_ksplit2 "), text
     rc, text = gb.gemm_f32_describe(-1, 3072, 3072, 3072, FAKE, 3072, FAKE, ldb, FAKE, 3072)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16_sk "), text
-    rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
+    rc, text = gb.gemm_f32_describe(-1, 1100, 1100, 1100, FAKE, 1100, FAKE, ldb, FAKE, 1100)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4_sk "), text
+    rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4 ") and "strip_rows=1" in text, text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 500, FAKE, 500, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_sk "), text
     k64 = gb.config_names().index("dma_64x64x64")
@@ -162,9 +164,14 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1000, 1000, 1000), "dma_64x64x32_ksplit4 "), ((512, 512, 1024), "dma_64x64x32_ksplit4 "),
     # K <= 512: no K split
     ((512, 512, 512), "dma_64x64x64 "), ((1000, 1000, 300), "dma_64x64x64 "),
-    # 272, 289 and 576 64 x 64 tiles: the last round would be under half
-    # full; stream-K over the K-split tile.  400 tiles: 64 x 64 tiles
-    ((1025, 1023, 1000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
+    # 272 tiles, 16 of them for a last row of 1-4 rows (rows x K <= 4096): one
+    # round of K-split tiles and a strip of FMAs
+    ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((1028, 1000, 1000), "dma_64x64x32_ksplit4 "),
+    ((1025, 1023, 2048), "dma_64x64x32_ksplit4_sk "), ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "),
+    # 272, 289, 324 and 576 64 x 64 tiles: the last round would be under
+    # half full; stream-K over the K-split tile.  400 tiles: 64 x 64 tiles
+    ((1025, 1023, 3000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
+    ((1100, 1100, 1100), "dma_64x64x32_ksplit4_sk "),
     ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "), ((1280, 1280, 1280), "dma_64x64x64 "),
     ((1025, 1023, 300), "dma_64x64x64_sk "),
     # two balanced rounds: the pipelined K split for K >= 2048, else 64 x 64

@@ -382,17 +382,17 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
     workers' atomic adds) and no memset: it captures into a HIP graph whose
     replays reproduce the eager result bit for bit, and two calls running at
     once on different streams share nothing."""
-    A, B = operands("uniform", 1025, 1023, 1000)
+    M, N, K = 1100, 1100, 1100
+    A, B = operands("uniform", M, N, K)
     dA = torch.from_numpy(A).to(dev)
     dB = torch.from_numpy(B).to(dev)
-    rc, desc = gb.gemm_f32_describe(-1, 1025, 1023, 1000, dA.data_ptr(), 1000, dB.data_ptr(), 1023,
-                                    dA.data_ptr(), 1023)
+    rc, desc = gb.gemm_f32_describe(-1, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dA.data_ptr(), N)
     assert desc.startswith("dma_64x64x32_ksplit4_sk "), desc
-    say("stream-K eager, graph and concurrent streams, 1025x1023x1000")
+    say(f"stream-K eager, graph and concurrent streams, {M}x{N}x{K}")
     eager = gb.matmul(dA, dB)
     torch.cuda.synchronize()
     assert_close(eager.cpu().numpy(), oracle.gemm(A, B), "stream-K eager")
-    out = torch.full((1025, 1023), float("nan"), device=dev)
+    out = torch.full((M, N), float("nan"), device=dev)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -408,7 +408,7 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
         torch.cuda.synchronize()
         assert torch.equal(out, eager)
     streams = [torch.cuda.Stream() for _ in range(2)]
-    outs = [torch.full((1025, 1023), float("nan"), device=dev) for _ in range(2)]
+    outs = [torch.full((M, N), float("nan"), device=dev) for _ in range(2)]
     torch.cuda.synchronize()
     for _ in range(4):
         for st, o in zip(streams, outs):
@@ -417,6 +417,34 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, eager)
+
+
+# ---------------------------------------------------------------------------
+# Remainder strips: 1-4 rows below one round of K-split tiles, computed with
+# FMAs by the last tile row's workgroups.
+# ---------------------------------------------------------------------------
+STRIP = [(1025, 1023, 1000), (1028, 1000, 1000), (1026, 1001, 1001), (1027, 1024, 1300)]
+
+
+@pytest.mark.parametrize("shape", STRIP, ids=lambda s: "x".join(map(str, s)))
+def test_strip_rows_bit_exact_and_padding_kept(dev, shape):
+    M, N, K = shape
+    rc, desc = gb.gemm_f32_describe(-1, M, N, K, 16, K + 3, 16, N + 1, 16, N + 5)
+    assert rc == gb.GEMM_F32_OK and desc.endswith(f" strip_rows={M % 64}"), desc
+    A, B = operands("quarter", M, N, K)
+    got, full = gpu_gemm(A, B, -1, dev, pad=(3, 1, 5))
+    assert_bit_exact(got, oracle.gemm(A, B), f"{shape} strip")
+    body = full[:M * (N + 5)].reshape(M, N + 5)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 5):]).all()
+
+
+def test_strip_rows_uniform_within_tolerance_and_deterministic(dev):
+    A, B = operands("uniform", 1026, 1001, 1001)
+    first, _ = gpu_gemm(A, B, -1, dev)
+    assert_close(first, oracle.gemm(A, B), "strip uniform")
+    for _ in range(2):
+        again, _ = gpu_gemm(A, B, -1, dev)
+        assert_bit_exact(again, first, "strip repeat")
 
 
 # ---------------------------------------------------------------------------
