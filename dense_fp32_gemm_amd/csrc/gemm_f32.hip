@@ -677,6 +677,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             constexpr int kGapFit = (kMfma - kReads) * (Q - 1) / kLoads;
             constexpr int kGap = kGapFit < 3 ? (kGapFit < 1 ? 1 : kGapFit) : 3;
             constexpr int kPerBlock = (kMfma - kReads) / kGap;   // panel loads per k-group
+            // The per-round barrier is a workgroup barrier, so only a tile
+            // with a single group (KS == 1) may use it: K-split groups can
+            // have different round counts, and one-wave groups (NW == 1)
+            // therefore run their rounds without any barrier.
             static_assert((KS == 1 || NW == 1) && S == 2 && Q % 2 == 0 && NL == NW && kEvenA && kEvenB,
                           "pipelined rounds: one group of all-loading waves, or one-wave groups; two buffers; "
                           "even k-group count");
