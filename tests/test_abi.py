@@ -155,7 +155,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
 @pytest.mark.parametrize("shape,name", [
     ((8192, 8192, 8192), "dma_256x256x32_pipe "), ((2048, 2048, 2048), "dma_128x128x64_pipe "),
     ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x64_pipe "),
-    ((8192, 8192, 128), "dma_128x128x16 "),
+    ((8192, 8192, 128), "dma_128x128x16_pipe "), ((8192, 8192, 512), "dma_128x128x16_pipe "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # at most one 64 x 64 tile per CU: K split inside the workgroup, 8
     # pipelined one-wave groups from K = 2048 on
