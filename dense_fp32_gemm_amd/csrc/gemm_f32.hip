@@ -1375,7 +1375,9 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    16 waves of 64 x 64; 4096 x 4096 x 16384: 3.66 against 3.72);
 //  * at least one 128 x 128 tile per CU: 128 x 128 with 4 pipelined waves
 //    of 64 x 64, 64-deep panels (2048^3: 125 us against 133 for 16 waves in
-//    two K-split groups);
+//    two K-split groups); with two or more balanced rounds and K < 2048,
+//    16-deep panels and three workgroups per CU instead (4096 x 3072 x
+//    1024: 185 us against 193; but 4096 x 2048 x 2048: 250 against 247);
 //  * at least three quarters of the CUs busy with 128 x 128 tiles while
 //    64 x 64 tiles would leave the last round mostly idle: the pipelined
 //    128 x 128 tile too (1792^3: 110 us against 121 for 64 x 64);
@@ -1430,8 +1432,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip)
         return unbalanced(kCfgDma256x256K32P) ? kCfgDma256x256K32PSK : kCfgDma256x256K32P;
     const int64_t t128 = tiles(kCfgDma128x128K64P);
     if (t128 >= kComputeUnits) {
-        if (!unbalanced(kCfgDma128x128K64P))
+        if (!unbalanced(kCfgDma128x128K64P)) {
+            // Two or more rounds with K < 2048: three resident workgroups of
+            // the 16-deep pipelined tile overlap each other's start-up and
+            // stores (6000 x 2000 x 1000: 185 us against 198).
+            if (t128 >= 2 * kComputeUnits && K < 2048)
+                return kCfgDma128x128K16P;
             return deep_ok ? kCfgDma128x128K64P : kCfgDma128x128K32S2;
+        }
         // Stream-K's extra launch and split-tile passes pay off over a long
         // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
         if (K >= 2048)

@@ -181,6 +181,10 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # 400, 576 and 576 128 x 128 tiles, K >= 2048: stream-K over them
     ((2560, 2560, 2560), "dma_128x128x64_pipe_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_sk "),
     ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "),
+    # two or more balanced rounds of 128 x 128 tiles: 16-deep pipelined
+    # panels for K < 2048
+    ((6000, 2000, 1000), "dma_128x128x16_pipe "), ((4096, 3072, 1024), "dma_128x128x16_pipe "),
+    ((4096, 2048, 2048), "dma_128x128x64_pipe "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe "),
 ])
