@@ -273,6 +273,43 @@ def test_graph_capture_replays_match_eager(dev):
         assert torch.equal(zout, torch.zeros_like(zout))
 
 
+GRAPH_PLANS = [((2048, 2048, 256), "dma_128x128x64_pipe "), ((4096, 4096, 128), "dma_128x128x16_pipe "),
+               ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((4096, 64, 2048), "dma_64x64x16_ksplit8_pipe ")]
+
+
+@pytest.mark.parametrize("shape,name", GRAPH_PLANS, ids=[n.strip() for _, n in GRAPH_PLANS])
+def test_graph_capture_of_each_kernel_family(dev, shape, name):
+    """The software-pipelined tiles, the one-wave K-split tile and the
+    remainder-strip kernel capture into a HIP graph like the rest: three
+    replays, with eager work and synchronisations between them, each equal
+    to the eager result bit for bit."""
+    M, N, K = shape
+    A, B = operands("uniform", M, N, K)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    rc, desc = gb.gemm_f32_describe(-1, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dA.data_ptr(), N)
+    assert rc == gb.GEMM_F32_OK and desc.startswith(name), desc
+    say(f"graph capture {desc}")
+    eager = gb.matmul(dA, dB)
+    out = torch.full((M, N), float("nan"), device=dev)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gb.matmul(dA, dB, out=out)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        gb.matmul(dA, dB, out=out)
+    for _ in range(3):
+        out.fill_(float("nan"))
+        other = gb.matmul(dB[:64, :64].contiguous(), dA[:64, :64].contiguous())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager)
+        del other
+
+
 def test_long_k_quarter_step_bit_exact(dev):
     """K = 2^20 - 16, the longest K for which quarter-step sums stay exact in
     binary32 (|partial sums| < 2^20 at 1/16 resolution), on the skinny path."""
