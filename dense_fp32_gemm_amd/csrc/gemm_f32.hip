@@ -60,6 +60,9 @@ struct GemmArgs {
     int strip_rows;      // rows M - strip_rows .. M-1 lie below the tile grid
                          // (tiles_m * BM = M - strip_rows): the last tile
                          // row's workgroups compute them with FMAs
+    int strip_cols;      // likewise columns N - strip_cols .. N-1, right of
+                         // the grid, for the last tile column (not together
+                         // with strip_rows)
 };
 
 // Most rows a remainder strip may hold, and its largest K: the strip's rows
@@ -195,7 +198,9 @@ template <class T>
 constexpr bool strip_fits()
 {
     constexpr int stage = T::BM * T::BK + T::BK * T::BN;
-    constexpr int red = T::kThreads / T::BN * kMaxStripRows * T::BN;
+    constexpr int red_rows = T::kThreads / T::BN * kMaxStripRows * T::BN;
+    constexpr int red_cols = T::BM * kMaxStripRows * kWaveSize;
+    constexpr int red = red_rows > red_cols ? red_rows : red_cols;
     return T::kThreads % T::BN == 0 && red + kMaxStripRows * kMaxStripK <= T::kSplit * T::kStages * stage;
 }
 static_assert(strip_fits<StripTile>(), "strip space in the strip tile's panel buffers");
@@ -992,6 +997,76 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             }
             __syncthreads();
         }
+
+        // The same for columns right of the grid: the workgroups of the last
+        // tile column compute columns N-strip_cols .. N-1 of their rows.  The
+        // strip's columns of B are copied to LDS as rows ([c][k]).  Each wave
+        // takes BM / waves consecutive rows; the lanes of a wave split K
+        // (lane l takes k = l, l+64, ...), so A is read along its rows.  Each
+        // lane sums its k's in order, then one thread per output adds the 64
+        // lanes' sums in lane order through LDS.
+        if constexpr (STRIP)
+        if (g.strip_cols > 0 && tn == g.tiles_n - 1) {
+            constexpr int kWaves = T::kThreads / kWaveSize;
+            constexpr int kRowsPerWave = BM / kWaves;
+            constexpr int kRed = BM * kMaxStripRows * kWaveSize;        // floats of partial sums
+            static_assert(BM % kWaves == 0 && kRowsPerWave >= 1, "column strip rows");
+            const int w = tid / kWaveSize;
+            const int c0 = g.N - g.strip_cols;
+            float *red = &lds[0][0][0];
+            float *sb = red + kRed;                  // strip_cols x K floats of B, as [c][k]
+            __syncthreads();
+            for (int e = tid; e < g.strip_cols * g.K; e += T::kThreads)
+                sb[e] = g.B[(int64_t)(e % g.K) * g.ldb + c0 + e / g.K];
+            __syncthreads();
+            float part[kRowsPerWave][kMaxStripRows] = {};
+            // Rows past M-1 (in the last tile row) read row M-1 instead;
+            // their sums are never stored.
+            const float *arow[kRowsPerWave];
+#pragma unroll
+            for (int rr = 0; rr < kRowsPerWave; ++rr)
+                arow[rr] = g.A + (int64_t)min(m0 + w * kRowsPerWave + rr, g.M - 1) * g.lda;
+            auto strip_sum = [&](auto cols) {
+                constexpr int CC = decltype(cols)::value;
+#pragma unroll 4
+                for (int k = lane; k < g.K; k += kWaveSize) {
+                    float a[kRowsPerWave];
+#pragma unroll
+                    for (int rr = 0; rr < kRowsPerWave; ++rr)
+                        a[rr] = arow[rr][k];
+#pragma unroll
+                    for (int c = 0; c < CC; ++c) {
+                        const float b = sb[c * g.K + k];
+#pragma unroll
+                        for (int rr = 0; rr < kRowsPerWave; ++rr)
+                            part[rr][c] = fmaf(a[rr], b, part[rr][c]);
+                    }
+                }
+            };
+            switch (g.strip_cols) {
+            case 1: strip_sum(std::integral_constant<int, 1>()); break;
+            case 2: strip_sum(std::integral_constant<int, 2>()); break;
+            case 3: strip_sum(std::integral_constant<int, 3>()); break;
+            default: strip_sum(std::integral_constant<int, 4>()); break;
+            }
+#pragma unroll
+            for (int rr = 0; rr < kRowsPerWave; ++rr)
+#pragma unroll
+                for (int c = 0; c < kMaxStripRows; ++c)
+                    red[((w * kRowsPerWave + rr) * kMaxStripRows + c) * kWaveSize + lane] = part[rr][c];
+            __syncthreads();
+            for (int e = tid; e < BM * kMaxStripRows; e += T::kThreads) {
+                const int row = e / kMaxStripRows, c = e % kMaxStripRows;
+                if (c < g.strip_cols && m0 + row < g.M) {
+                    const float *v = &red[e * kWaveSize];
+                    float sum = v[0];
+                    for (int l = 1; l < kWaveSize; ++l)
+                        sum += v[l];
+                    store_c(&cbase[(int64_t)(m0 + row) * g.ldc + c0 + c], sum);
+                }
+            }
+            __syncthreads();
+        }
     };
 
     if (SPLIT) {
@@ -1409,9 +1484,9 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 // dimensions) the 32-deep alternatives are chosen instead.  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
-int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip)
+int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_rows, int &strip_cols)
 {
-    strip = 0;
+    strip_rows = strip_cols = 0;
     if (M < 16 || N < 16)
         return kCfgValu64;
     auto tiles = [&](int c) { return ceil_div(M, kConfigs[c].bm) * ceil_div(N, kConfigs[c].bn); };
@@ -1466,7 +1541,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip)
     static_assert(std::is_same<Tile64x64K32S4, StripTile>::value, "the strip tile is the 4-group K-split tile");
     if (K > 512 && K < kMaxStripK && M % 64 != 0 && (M % 64) * K <= 4096 && t_full <= kComputeUnits &&
         t32 > kComputeUnits) {
-        strip = M % 64;
+        strip_rows = M % 64;
+        return kCfgDma64x64K32S4;
+    }
+    // The same for a last tile column of at most kMaxStripRows columns.
+    const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
+    if (K > 512 && K < kMaxStripK && N % 64 != 0 && (N % 64) * K <= 4096 && t_full_n <= kComputeUnits &&
+        t32 > kComputeUnits) {
+        strip_cols = N % 64;
         return kCfgDma64x64K32S4;
     }
     if (K > 512 && t32 <= kComputeUnits)
@@ -1502,6 +1584,7 @@ struct Plan {
     int tiles_m, tiles_n;
     int grid;
     int strip_rows;      // rows below the tile grid, computed as a strip
+    int strip_cols;      // columns right of it, computed as a strip
 };
 
 // Validates the arguments (sizes, leading dimensions, configuration index,
@@ -1519,7 +1602,7 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     plan->config = -1;
     plan->vec_a = plan->vec_b = false;
     plan->tiles_m = plan->tiles_n = plan->grid = 0;
-    plan->strip_rows = 0;
+    plan->strip_rows = plan->strip_cols = 0;
     if (M == 0 || N == 0)
         return GEMM_F32_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr)))
@@ -1531,25 +1614,26 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
         return GEMM_F32_OK;
     }
     int c = config;
-    int strip = 0;
+    int strip = 0, strip_c = 0;
     if (c < 0) {
         // The rule's direct-to-LDS choice; if its panels are too tall or deep
         // for 32-bit offsets at these leading dimensions, its choice among
         // 32-deep panels, and failing that the register-staged kernel.
-        c = select_config(M, N, K, true, true, strip);
+        c = select_config(M, N, K, true, true, strip, strip_c);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, true, false, strip);
+            c = select_config(M, N, K, true, false, strip, strip_c);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, false, false, strip);
+            c = select_config(M, N, K, false, false, strip, strip_c);
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
     const int64_t tm = strip ? (M - strip) / kConfigs[c].bm : ceil_div(M, kConfigs[c].bm);
-    const int64_t tn = ceil_div(N, kConfigs[c].bn);
+    const int64_t tn = strip_c ? (N - strip_c) / kConfigs[c].bn : ceil_div(N, kConfigs[c].bn);
     if (tm * tn > INT32_MAX)
         return GEMM_F32_ERR_DIM;
     plan->config = c;
     plan->strip_rows = strip;
+    plan->strip_cols = strip_c;
     plan->tiles_m = (int)tm;
     plan->tiles_n = (int)tn;
     if (kConfigs[c].streamk)
@@ -1599,9 +1683,10 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     g.slices = 1;
     g.slab = 0;
     g.strip_rows = p.strip_rows;
+    g.strip_cols = p.strip_cols;
     // A plan with a remainder strip runs the strip tile's strip kernel (the
     // rule pairs strips with that tile only).
-    const hipError_t err = p.strip_rows > 0
+    const hipError_t err = p.strip_rows > 0 || p.strip_cols > 0
                                ? LaunchDma<StripTile, false, false, true>::run(g, true, true, p.grid, stream)
                                : kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
@@ -1665,7 +1750,7 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     g.tiles_n = (int)ceil_div(N, TileSplitK::BN);
     g.slices = slices;
     g.slab = (int64_t)M * N;
-    g.strip_rows = 0;
+    g.strip_rows = g.strip_cols = 0;
     const int grid = g.tiles_m * g.tiles_n * slices;
     hipError_t err = LaunchDma<TileSplitK, false, true>::run(g, true, true, grid, stream);
     if (err != hipSuccess)
@@ -1763,6 +1848,8 @@ int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
                                kConfigs[p.config].threads, p.vec_a ? "x4" : "x1", p.vec_b ? "x4" : "x1");
         if (p.strip_rows > 0 && n >= 0 && n < buflen)
             snprintf(buf + n, (size_t)(buflen - n), " strip_rows=%d", p.strip_rows);
+        else if (p.strip_cols > 0 && n >= 0 && n < buflen)
+            snprintf(buf + n, (size_t)(buflen - n), " strip_cols=%d", p.strip_cols);
     }
     return rc;
 }

@@ -148,7 +148,8 @@ GEMM_F32_API int gemm_f32_config_info(int config, int *bm, int *bn, int *bk,
  * these arguments (config -1: what gemm_f32() would enqueue): the
  * configuration name first ("none" for an empty output, "fill_zero" for
  * K == 0), then tile grid, workgroup count and load widths, and, when the
- * last 1-4 rows are computed as a strip below the tile grid, " strip_rows=R".
+ * last 1-4 rows or columns are computed as a strip beside the tile grid,
+ * " strip_rows=R" or " strip_cols=C".
  * Pointers are only inspected for alignment, never dereferenced.  Returns the
  * status the call would return for the same arguments.
  */

@@ -168,6 +168,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # round of K-split tiles and a strip of FMAs
     ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((1028, 1000, 1000), "dma_64x64x32_ksplit4 "),
     ((1025, 1023, 2048), "dma_64x64x32_ksplit4_sk "), ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "),
+    ((1023, 1025, 1000), "dma_64x64x32_ksplit4 "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
     # 272, 289, 324 and 576 64 x 64 tiles: the last round would be under
     # half full; stream-K over the K-split tile.  400 tiles: 64 x 64 tiles
     ((1025, 1023, 3000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),

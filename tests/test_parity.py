@@ -460,14 +460,17 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
 # Remainder strips: 1-4 rows below one round of K-split tiles, computed with
 # FMAs by the last tile row's workgroups.
 # ---------------------------------------------------------------------------
-STRIP = [(1025, 1023, 1000), (1028, 1000, 1000), (1026, 1001, 1001), (1027, 1024, 1300)]
+STRIP = [((1025, 1023, 1000), "strip_rows=1"), ((1028, 1000, 1000), "strip_rows=4"),
+         ((1026, 1001, 1001), "strip_rows=2"), ((1027, 1024, 1300), "strip_rows=3"),
+         ((1023, 1025, 1000), "strip_cols=1"), ((1000, 1028, 1000), "strip_cols=4"),
+         ((1001, 1026, 1001), "strip_cols=2"), ((1024, 1027, 1300), "strip_cols=3")]
 
 
-@pytest.mark.parametrize("shape", STRIP, ids=lambda s: "x".join(map(str, s)))
-def test_strip_rows_bit_exact_and_padding_kept(dev, shape):
+@pytest.mark.parametrize("shape,strip", STRIP, ids=["x".join(map(str, s)) for s, _ in STRIP])
+def test_strips_bit_exact_and_padding_kept(dev, shape, strip):
     M, N, K = shape
     rc, desc = gb.gemm_f32_describe(-1, M, N, K, 16, K + 3, 16, N + 1, 16, N + 5)
-    assert rc == gb.GEMM_F32_OK and desc.endswith(f" strip_rows={M % 64}"), desc
+    assert rc == gb.GEMM_F32_OK and desc.endswith(" " + strip), desc
     A, B = operands("quarter", M, N, K)
     got, full = gpu_gemm(A, B, -1, dev, pad=(3, 1, 5))
     assert_bit_exact(got, oracle.gemm(A, B), f"{shape} strip")
@@ -475,13 +478,14 @@ def test_strip_rows_bit_exact_and_padding_kept(dev, shape):
     assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 5):]).all()
 
 
-def test_strip_rows_uniform_within_tolerance_and_deterministic(dev):
-    A, B = operands("uniform", 1026, 1001, 1001)
+@pytest.mark.parametrize("shape", [(1026, 1001, 1001), (1001, 1026, 1001)], ids=["rows", "cols"])
+def test_strips_uniform_within_tolerance_and_deterministic(dev, shape):
+    A, B = operands("uniform", *shape)
     first, _ = gpu_gemm(A, B, -1, dev)
-    assert_close(first, oracle.gemm(A, B), "strip uniform")
+    assert_close(first, oracle.gemm(A, B), f"strip uniform {shape}")
     for _ in range(2):
         again, _ = gpu_gemm(A, B, -1, dev)
-        assert_bit_exact(again, first, "strip repeat")
+        assert_bit_exact(again, first, f"strip repeat {shape}")
 
 
 # ---------------------------------------------------------------------------
