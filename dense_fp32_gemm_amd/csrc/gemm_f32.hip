@@ -1732,7 +1732,13 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
         return run(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
     const int slices = splitk_slices(M, N, K);
     const size_t need = splitk_bytes(M, N, K);
-    const ConfigInfo &cfg = kConfigs[kCfgDma64x64K32S4];
+    // Slices of at least 2048 of K run the pipelined 8-group K-split tile
+    // (640 x 640 x 8192, two slices: 74 us against 83; 512 x 512 x 8192:
+    // 45 against 47), shorter ones the 4-group tile (130 x 70 x 5000, 19
+    // slices: 21.6 us against 25).  Both cover the same 64 x 64 tiles.
+    static_assert(Tile64x64K16S8P::BM == TileSplitK::BM && Tile64x64K16S8P::BN == TileSplitK::BN, "same tiles");
+    const bool pipe = K / slices >= 2048;
+    const ConfigInfo &cfg = kConfigs[pipe ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4];
     if (slices < 2 || ws == nullptr || ws_bytes < need || ((uintptr_t)ws & 15u) ||
         !dma_offsets_fit(cfg, lda, ldb))
         return run(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);
@@ -1752,7 +1758,8 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     g.slab = (int64_t)M * N;
     g.strip_rows = g.strip_cols = 0;
     const int grid = g.tiles_m * g.tiles_n * slices;
-    hipError_t err = LaunchDma<TileSplitK, false, true>::run(g, true, true, grid, stream);
+    hipError_t err = pipe ? LaunchDma<Tile64x64K16S8P, false, true>::run(g, true, true, grid, stream)
+                          : LaunchDma<TileSplitK, false, true>::run(g, true, true, grid, stream);
     if (err != hipSuccess)
         return GEMM_F32_ERR_LAUNCH;
     const int64_t elems = (int64_t)M * N;

@@ -510,7 +510,8 @@ def gpu_gemm_ws(A, B, dev, ws_bytes=None, ldc_pad=0):
     return np.ascontiguousarray(full[:M * ldc].reshape(M, ldc)[:, :N]), full, ws.cpu().numpy(), need
 
 
-SPLITK = [(200, 200, 20000), (130, 70, 5000), (64, 300, 3000), (17, 1000, 4096), (600, 600, 4096)]
+SPLITK = [(200, 200, 20000), (130, 70, 5000), (64, 300, 3000), (17, 1000, 4096), (600, 600, 4096),
+          (640, 650, 8190)]
 
 
 @pytest.mark.parametrize("shape", SPLITK, ids=lambda s: "x".join(map(str, s)))
