@@ -1210,9 +1210,11 @@ __global__ __launch_bounds__(256) void fill_zero(float *C, int64_t ldc, int M, i
 // ---------------------------------------------------------------------------
 // Configurations
 // ---------------------------------------------------------------------------
-// Tile shapes: BM x BN output tile, BK = 16 panel depth, WAVES_M x WAVES_N
+// Tile shapes (MfmaTile<BM, BN, BK, WAVES_M, WAVES_N, KSPLIT, STAGES, GROUP,
+// LOADERS, PIPE>): BM x BN output tile, BK-deep K-panels, WAVES_M x WAVES_N
 // waves each owning a (BM/WAVES_M) x (BN/WAVES_N) block; optional K-split
-// groups and panel-ring depth.
+// groups, panel-ring depth, loader-wave count and the software-pipelined
+// round loop.
 using Tile256x256W16 = MfmaTile<256, 256, 16, 4, 4, 1, 2, 8, 8>;    // 16 waves of 64 x 64, 8 load
 using Tile128x128W16 = MfmaTile<128, 128, 16, 4, 4, 1, 2, 8, 8>;    // 16 waves of 32 x 32, 8 load
 using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;       // 4 waves of 64 x 64
