@@ -841,12 +841,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         __syncthreads();
 
         if (KS > 1) {
-            // Fold the groups' partial sums into group 0 in a fixed order
-            // (group 1, then 2, ...), through LDS laid out as C's tile.  The
-            // panel buffers are free: the loop ended with a barrier.
-            float *red = &lds[0][0][0];
-            for (int src = 1; src < KS; ++src) {
-                if (group == src) {
+            // Fold the groups' partial sums into group 0 along a fixed binary
+            // tree, through LDS laid out as C's tile: at distance d = 1, 2,
+            // 4, ... group g with g % 2d == d hands its sum to group g - d
+            // through a region of its own, so each step's additions run in
+            // parallel and their order never changes (8 one-wave groups:
+            // 16384 x 64 x 4096 67.8 us against 68.6 for folding one group
+            // after another).  The panel buffers are free: the loop ended
+            // with a barrier.
+            static_assert((KS & (KS - 1)) == 0, "tree fold over a power-of-two number of groups");
+            static_assert(KS / 2 * BM * BN <= KS * S * kStage, "fold regions fit in the panel buffers");
+            for (int d = 1; d < KS; d *= 2) {
+                float *red = &lds[0][0][0] + (group / (2 * d)) * (BM * BN);
+                if (group % (2 * d) == d) {
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -858,7 +865,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                             }
                 }
                 __syncthreads();
-                if (group == 0) {
+                if (group % (2 * d) == 0) {
 #pragma unroll
                     for (int i = 0; i < FM; ++i)
 #pragma unroll
