@@ -11,8 +11,8 @@ a device synchronisation on both sides; HIP events around each call on the
 stream it is enqueued on give the per-launch kernel time used for the
 roofline.  Every run also times 2048^3, the metric's second size, and
 reports it inside ``config``; ``--table`` adds every other workload shape (on
-stderr).  Short kernels get at least 0.2 s of warm-up so they are not timed
-while the clock ramps up.  The last stdout line is one JSON object.
+stderr).  Every workload gets at least 0.2 s of warm-up calls, so a short
+kernel is not timed while the clock ramps up.  The last stdout line is one JSON object.
 """
 from __future__ import annotations
 
@@ -199,7 +199,7 @@ def main():
         del src, dst
 
     M, N, K = args.shape
-    head = time_gemm(torch, gb, M, N, K, args.steps, args.warmup, args.config)
+    head = time_gemm(torch, gb, M, N, K, args.steps, args.warmup, args.config, min_warm_s=0.2)
     log(json.dumps(head))
     peak = gb.gemm_f32_device_peak(0)
     log(f"derived FP32 matrix peak: {peak['compute_units']} CUs x 256 FLOP/clk x "
