@@ -5,7 +5,7 @@
 //
 // Kernels:
 //
-//  * gemm_f32_mfma_dma<Tile, SK, SPLIT>: the main kernel.  One workgroup per
+//  * gemm_f32_mfma_dma<Tile, SK, SPLIT, STRIP, WB>: the main kernel.  One workgroup per
 //    BM x BN tile of C; K is walked in BK-deep panels that buffer loads write
 //    straight into a ring of LDS buffers, so later panels are fetched while
 //    the matrix cores work on the current one (one barrier per panel).  Each
@@ -16,7 +16,9 @@
 //    128 x 128 or 64 x 64) and the K-split tile of one-wave groups run a
 //    software-pipelined round loop (PIPE) that interleaves fragment reads
 //    and panel loads with the MFMAs.  Ragged edges are zero-filled on load
-//    and masked on store, so every shape runs on this path.
+//    and masked on store, so every shape runs on this path.  C is written
+//    with streaming stores, or (WB twins, for a large C whose rows are not
+//    16-byte aligned) with ordinary write-back stores.
 //  * gemm_f32_mfma<Tile, VEC_A, VEC_B>: the same tiling with panels staged
 //    global -> VGPR -> LDS, for rows too long for 32-bit buffer offsets.
 //  * gemm_f32_valu: a 64 x 64 LDS-tiled vector-FMA kernel (4 x 4 outputs per
@@ -114,13 +116,29 @@ __device__ inline void streamk_range(int b, int workers, int64_t iters, int64_t 
 }
 
 // Epilogue store of one C element.  C is written once and not read again by
-// the kernel, so the store is marked non-temporal: it streams to memory
-// instead of displacing the A and B panels other workgroups still read from
-// L2 (measured +1 % on the store-heavy 8192 x 8192 x 128 and on 2048^3).
+// the kernel, so the store is normally marked non-temporal: it streams to
+// memory instead of displacing the A and B panels other workgroups still read
+// from L2 (measured +1 % on the store-heavy 8192 x 8192 x 128 and on 2048^3).
+// With WB (write-back) it is an ordinary store instead: when C's rows are
+// not 16-byte aligned, the 128-byte row pieces a store instruction writes
+// straddle cache lines, and for a large C streamed partial lines cost far
+// more than lines completed in L2 before they are written back
+// (4119 x 4789 x 77: 40.6 us against 70.8; 8191 x 8191 x 128: 162 against
+// 212).
+template <bool WB = false>
 __device__ inline void store_c(float *p, float v)
 {
-    __builtin_nontemporal_store(v, p);
+    if constexpr (WB)
+        *p = v;
+    else
+        __builtin_nontemporal_store(v, p);
 }
+
+// Elements of C from which rows that are not 16-byte aligned are written
+// with ordinary stores (the WB kernel instances); below it the partial lines
+// still stream (1023 x 1025 x 1000: 28.9 us against 30.7 with ordinary
+// stores).  2^23 floats are 32 MiB, the eight L2 caches together.
+constexpr int64_t kWriteBackFromElems = int64_t(1) << 23;
 
 // ---------------------------------------------------------------------------
 // Guarded loads: 4 consecutive elements of one row, +0.0 outside the matrix.
@@ -397,7 +415,7 @@ __device__ inline void buffer_to_lds(__amdgpu_buffer_rsrc_t rsrc, float *lds_bas
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, offset, 0, 0, 0);
 }
 
-template <class T, bool SK = false, bool SPLIT = false, bool STRIP = false>
+template <class T, bool SK = false, bool SPLIT = false, bool STRIP = false, bool WB = false>
 __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 {
     constexpr int BM = T::BM, BN = T::BN, BK = T::BK;
@@ -930,7 +948,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                             if (shared)
                                 unsafeAtomicAdd(c, acc[i][j][r]);
                             else
-                                store_c(c, acc[i][j][r]);
+                                store_c<WB>(c, acc[i][j][r]);
                         }
                     }
                 }
@@ -1321,11 +1339,11 @@ struct PlainKernel {
 // The direct-to-LDS kernel has one instance per tile and mode: it loads 16
 // bytes per lane from any 4-byte aligned operand, so the load-width flags
 // of the plan do not apply to it.
-template <class T, bool SK = false, bool SPLIT = false, bool STRIP = false>
+template <class T, bool SK = false, bool SPLIT = false, bool STRIP = false, bool WB = false>
 struct LaunchDma {
     static hipError_t run(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
     {
-        hipLaunchKernelGGL((gemm_f32_mfma_dma<T, SK, SPLIT, STRIP>), dim3(grid), dim3(T::kThreads), 0, s, g);
+        hipLaunchKernelGGL((gemm_f32_mfma_dma<T, SK, SPLIT, STRIP, WB>), dim3(grid), dim3(T::kThreads), 0, s, g);
         return hipGetLastError();
     }
     static int occupancy()
@@ -1340,7 +1358,7 @@ struct LaunchDma {
 
 // Stream-K: clear the tiles two workgroups will share, then run the
 // workers (one per compute unit) on the same stream.
-template <class T>
+template <class T, bool WB = false>
 hipError_t launch_streamk(const GemmArgs &g, bool va, bool vb, int grid, hipStream_t s)
 {
     if (grid > 1) {
@@ -1349,7 +1367,7 @@ hipError_t launch_streamk(const GemmArgs &g, bool va, bool vb, int grid, hipStre
         if (e != hipSuccess)
             return e;
     }
-    return LaunchDma<T, true>::run(g, va, vb, grid, s);
+    return LaunchDma<T, true, false, false, WB>::run(g, va, vb, grid, s);
 }
 
 hipError_t launch_valu(const GemmArgs &g, bool, bool, int grid, hipStream_t s)
@@ -1373,32 +1391,43 @@ struct ConfigInfo {
     hipError_t (*launch)(const GemmArgs &, bool, bool, int, hipStream_t);
     int (*occupancy)();
     bool streamk;                // one worker per CU over all tiles' K-panels
+    // The instance with write-back C stores, for a large C whose rows are
+    // not 16-byte aligned (nullptr: none, the streaming one runs).
+    hipError_t (*launch_wb)(const GemmArgs &, bool, bool, int, hipStream_t);
 };
 
 template <class T>
 constexpr ConfigInfo config_staged(const char *name)
 {
     return {name, T::BM, T::BN, T::BK, T::kThreads, false, &Launch<T, PlainKernel>::run,
-            &Launch<T, PlainKernel>::occupancy, false};
+            &Launch<T, PlainKernel>::occupancy, false, nullptr};
 }
 
-template <class T>
+// WB: also build the write-back twin (only for the tiles the shape rule
+// picks for problems with a large C).
+template <class T, bool WB = false>
 constexpr ConfigInfo config_dma(const char *name)
 {
+    hipError_t (*wb)(const GemmArgs &, bool, bool, int, hipStream_t) = nullptr;
+    if constexpr (WB)
+        wb = &LaunchDma<T, false, false, false, true>::run;
     return {name, T::BM, T::BN, T::BK, T::kThreads, true, &LaunchDma<T>::run, &LaunchDma<T>::occupancy,
-            false};
+            false, wb};
 }
 
-template <class T>
+template <class T, bool WB = false>
 constexpr ConfigInfo config_streamk(const char *name)
 {
+    hipError_t (*wb)(const GemmArgs &, bool, bool, int, hipStream_t) = nullptr;
+    if constexpr (WB)
+        wb = &launch_streamk<T, true>;
     return {name, T::BM, T::BN, T::BK, T::kThreads, true, &launch_streamk<T>,
-            &LaunchDma<T, true>::occupancy, true};
+            &LaunchDma<T, true>::occupancy, true, wb};
 }
 
 // Indexed by ConfigId.
 const ConfigInfo kConfigs[kNumConfigs] = {
-    {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu, false},
+    {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu, false, nullptr},
     config_dma<Tile256x256W16>("dma_256x256x16_w16"),
     config_dma<Tile128x128W16>("dma_128x128x16_w16"),
     config_dma<Tile128x128>("dma_128x128x16"),
@@ -1412,25 +1441,25 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_staged<Tile64x64>("staged_64x64x16"),
     config_dma<Tile256x256K32W16>("dma_256x256x32_w16"),
     config_dma<Tile128x128K32W16>("dma_128x128x32_w16"),
-    config_dma<Tile64x64K32>("dma_64x64x32"),
+    config_dma<Tile64x64K32, true>("dma_64x64x32"),
     config_dma<Tile64x64K32S4>("dma_64x64x32_ksplit4"),
-    config_dma<Tile64x128K32>("dma_64x128x32"),
-    config_dma<Tile128x64K32>("dma_128x64x32"),
+    config_dma<Tile64x128K32, true>("dma_64x128x32"),
+    config_dma<Tile128x64K32, true>("dma_128x64x32"),
     config_dma<Tile128x128K32>("dma_128x128x32"),
-    config_streamk<Tile64x64K32>("dma_64x64x32_sk"),
+    config_streamk<Tile64x64K32, true>("dma_64x64x32_sk"),
     config_streamk<Tile128x128K32W16>("dma_128x128x32_w16_sk"),
     config_streamk<Tile256x256K32W16>("dma_256x256x32_w16_sk"),
     config_dma<Tile64x64K64>("dma_64x64x64"),
     config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
     config_dma<Tile128x128K32S2>("dma_128x128x32_ksplit2"),
-    config_dma<Tile256x256K32P>("dma_256x256x32_pipe"),
-    config_streamk<Tile256x256K32P>("dma_256x256x32_pipe_sk"),
-    config_dma<Tile128x128K64P>("dma_128x128x64_pipe"),
-    config_streamk<Tile128x128K64P>("dma_128x128x64_pipe_sk"),
-    config_dma<Tile64x64K16S8P>("dma_64x64x16_ksplit8_pipe"),
-    config_streamk<Tile64x64K16S8P>("dma_64x64x16_ksplit8_pipe_sk"),
+    config_dma<Tile256x256K32P, true>("dma_256x256x32_pipe"),
+    config_streamk<Tile256x256K32P, true>("dma_256x256x32_pipe_sk"),
+    config_dma<Tile128x128K64P, true>("dma_128x128x64_pipe"),
+    config_streamk<Tile128x128K64P, true>("dma_128x128x64_pipe_sk"),
+    config_dma<Tile64x64K16S8P, true>("dma_64x64x16_ksplit8_pipe"),
+    config_streamk<Tile64x64K16S8P, true>("dma_64x64x16_ksplit8_pipe_sk"),
     config_streamk<Tile64x64K32S4>("dma_64x64x32_ksplit4_sk"),
-    config_dma<Tile128x128K16P>("dma_128x128x16_pipe"),
+    config_dma<Tile128x128K16P, true>("dma_128x128x16_pipe"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1590,6 +1619,7 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 struct Plan {
     int config;
     bool vec_a, vec_b;
+    bool wb_c;           // run the configuration's write-back C-store twin
     int tiles_m, tiles_n;
     int grid;
     int strip_rows;      // rows below the tile grid, computed as a strip
@@ -1610,6 +1640,7 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
         return GEMM_F32_ERR_CONFIG;
     plan->config = -1;
     plan->vec_a = plan->vec_b = false;
+    plan->wb_c = false;
     plan->tiles_m = plan->tiles_n = plan->grid = 0;
     plan->strip_rows = plan->strip_cols = 0;
     if (M == 0 || N == 0)
@@ -1649,6 +1680,8 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
         plan->grid = (int)(tm * tn < kComputeUnits ? tm * tn : kComputeUnits);
     else
         plan->grid = (int)(tm * tn < kMaxGrid ? tm * tn : kMaxGrid);
+    plan->wb_c = kConfigs[c].launch_wb != nullptr && !strip && !strip_c &&
+                 !(aligned16(C) && ldc % 4 == 0) && (int64_t)M * N >= kWriteBackFromElems;
     if (kConfigs[c].dma) {
         // Direct-to-LDS loads move 16 bytes from any 4-byte aligned address
         // (checked on gfx950 together with the per-dword range check).  A
@@ -1697,7 +1730,8 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     // rule pairs strips with that tile only).
     const hipError_t err = p.strip_rows > 0 || p.strip_cols > 0
                                ? LaunchDma<StripTile, false, false, true>::run(g, true, true, p.grid, stream)
-                               : kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
+                           : p.wb_c ? kConfigs[p.config].launch_wb(g, p.vec_a, p.vec_b, p.grid, stream)
+                                    : kConfigs[p.config].launch(g, p.vec_a, p.vec_b, p.grid, stream);
     return err == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
@@ -1866,6 +1900,8 @@ int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
             snprintf(buf + n, (size_t)(buflen - n), " strip_rows=%d", p.strip_rows);
         else if (p.strip_cols > 0 && n >= 0 && n < buflen)
             snprintf(buf + n, (size_t)(buflen - n), " strip_cols=%d", p.strip_cols);
+        else if (p.wb_c && n >= 0 && n < buflen)
+            snprintf(buf + n, (size_t)(buflen - n), " c_store=write_back");
     }
     return rc;
 }

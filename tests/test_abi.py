@@ -118,6 +118,33 @@ def test_describe():
     assert "load_a=x1 load_b=x4" in text, text
 
 
+WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
+              "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
+              "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe", "dma_64x64x16_ksplit8_pipe_sk",
+              "dma_128x128x16_pipe"]
+
+
+def test_describe_write_back_c_stores():
+    """C with at least 2^23 elements and rows that are not 16-byte aligned
+    (ldc % 4 != 0, or a base 4 bytes off) runs the write-back twin of the
+    chosen tile; aligned rows, a smaller C or a tile without a twin stream."""
+    rc, text = gb.gemm_f32_describe(-1, 4119, 4789, 77, FAKE, 77, FAKE, 4789, FAKE, 4789)
+    assert rc == gb.GEMM_F32_OK and text.endswith("c_store=write_back"), text
+    rc, text = gb.gemm_f32_describe(-1, 4096, 4096, 77, FAKE, 77, FAKE, 4096, FAKE + 8, 4096)
+    assert text.endswith("c_store=write_back"), text
+    rc, text = gb.gemm_f32_describe(-1, 4096, 4096, 77, FAKE, 77, FAKE, 4096, FAKE, 4096)
+    assert "write_back" not in text, text
+    rc, text = gb.gemm_f32_describe(-1, 2048, 4095, 77, FAKE, 77, FAKE, 4095, FAKE, 4095)
+    assert "write_back" not in text, text          # 2048 * 4095 < 2^23 elements
+    rc, text = gb.gemm_f32_describe(-1, 2049, 4097, 40, FAKE, 40, FAKE, 4097, FAKE, 4097)
+    assert text.endswith("c_store=write_back"), text
+    names = gb.config_names()
+    for c, n in enumerate(names):
+        rc, text = gb.gemm_f32_describe(c, 2049, 4097, 40, FAKE, 40, FAKE, 4097, FAKE, 4097)
+        assert rc == gb.GEMM_F32_OK
+        assert ("c_store=write_back" in text) == (n in WRITE_BACK), (n, text)
+
+
 def test_wide_rows_fall_back_to_staged_kernels():
     """Direct-to-LDS kernels address a panel with 32-bit offsets; rows so long
     that a panel spans 2 GiB select the register-staged kernels instead, and

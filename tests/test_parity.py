@@ -184,6 +184,36 @@ def test_unaligned_bases(dev, config):
     assert np.isnan(full[:2]).all()
 
 
+WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
+              "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
+              "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe", "dma_64x64x16_ksplit8_pipe_sk",
+              "dma_128x128x16_pipe"]
+
+
+@functools.lru_cache(maxsize=1)
+def write_back_case():
+    M, N, K = 2049, 4097, 40          # M * N >= 2^23 elements
+    A, B = operands("quarter", M, N, K)
+    return A, B, oracle.gemm(A, B)
+
+
+@pytest.mark.parametrize("name", ["auto"] + WRITE_BACK)
+def test_write_back_c_stores_bit_exact_and_padding_kept(dev, name):
+    """A large C whose rows are not 16-byte aligned runs the tiles'
+    write-back twins (ordinary instead of streaming stores): bit-exact on
+    quarter-step operands, and C's row padding (NaN) untouched."""
+    config = -1 if name == "auto" else gb.config_names().index(name)
+    A, B, want = write_back_case()
+    M, K = A.shape
+    N = B.shape[1]
+    rc, text = gb.gemm_f32_describe(config, M, N, K, 4, K, 4, N, 4, N + 2)
+    assert text.endswith("c_store=write_back"), text
+    got, full = gpu_gemm(A, B, config, dev, pad=(0, 0, 2))
+    assert_bit_exact(got, want, f"{name} write-back C stores")
+    body = full[:M * (N + 2)].reshape(M, N + 2)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 2):]).all()
+
+
 def test_k_zero_writes_positive_zero(dev):
     A = np.zeros((37, 0), np.float32)
     B = np.zeros((0, 45), np.float32)
