@@ -1539,13 +1539,23 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
         const int64_t t = tiles(c);
         return 5 * t < 4 * ceil_div(t, kComputeUnits) * kComputeUnits;
     };
+    // Whether stream-K's even split beats whole tiles: over a long K its
+    // extra launch and split tiles cost about 3 %, so it pays once the last
+    // round leaves more than 4 % of the CU-rounds idle (7168 x 6656 x 4096,
+    // 95 % filled: 2688 us against 2785 for 256 x 256 tiles; 5000 x 2600 x
+    // 4096, 82 %: 813 against 954 for 128 x 128; but 3584 x 3456 x 4096,
+    // 98 %: 730 against 719); below K = 2048 only past a fifth.
+    auto streamk_pays = [&](int c) {
+        const int64_t t = tiles(c);
+        return K >= 2048 ? 25 * t < 24 * ceil_div(t, kComputeUnits) * kComputeUnits : unbalanced(c);
+    };
     if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128K16P;
     if (tiles(kCfgDma256x256K32P) >= kComputeUnits)
-        return unbalanced(kCfgDma256x256K32P) ? kCfgDma256x256K32PSK : kCfgDma256x256K32P;
+        return streamk_pays(kCfgDma256x256K32P) ? kCfgDma256x256K32PSK : kCfgDma256x256K32P;
     const int64_t t128 = tiles(kCfgDma128x128K64P);
     if (t128 >= kComputeUnits) {
-        if (!unbalanced(kCfgDma128x128K64P)) {
+        if (!streamk_pays(kCfgDma128x128K64P)) {
             // Two or more rounds with K < 2048: three resident workgroups of
             // the 16-deep pipelined tile overlap each other's start-up and
             // stores (6000 x 2000 x 1000: 185 us against 198).
@@ -1595,6 +1605,12 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     if (K > 512 && t32 <= 3 * kComputeUnits && 2 * last < kComputeUnits)
         return kCfgDma64x64K32S4SK;
     if (K >= 2048 && t32 <= 2 * kComputeUnits)
+        return kCfgDma64x64K16S8P;
+    // Three rounds with a fuller last one still favour the 8 pipelined
+    // groups once K is long (5932 x 460 x 4096: 200 us against 213 for
+    // 64 x 64 tiles of 4 waves; x 8192: 378 against 419; x 2048: 112
+    // against 110).
+    if (K >= 4096 && t32 <= 3 * kComputeUnits)
         return kCfgDma64x64K16S8P;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * kComputeUnits)
