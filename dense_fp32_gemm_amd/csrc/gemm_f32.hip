@@ -1543,16 +1543,26 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // extra launch and split tiles cost about 3 %, so it pays once the last
     // round leaves more than 4 % of the CU-rounds idle (7168 x 6656 x 4096,
     // 95 % filled: 2688 us against 2785 for 256 x 256 tiles; 5000 x 2600 x
-    // 4096, 82 %: 813 against 954 for 128 x 128; but 3584 x 3456 x 4096,
-    // 98 %: 730 against 719); below K = 2048 only past a fifth.
+    // 4096, 82 %: 813 against 954 for 128 x 128; 5120 x 5120 x 1536, 89 %:
+    // 598 against 627 for the 16-deep 128 x 128 tile; but 3584 x 3456 x
+    // 4096, 98 %: 730 against 719); below K = 1024 only past a fifth.
     auto streamk_pays = [&](int c) {
         const int64_t t = tiles(c);
-        return K >= 2048 ? 25 * t < 24 * ceil_div(t, kComputeUnits) * kComputeUnits : unbalanced(c);
+        return K >= 1024 ? 25 * t < 24 * ceil_div(t, kComputeUnits) * kComputeUnits : unbalanced(c);
     };
-    if (K <= 512 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
+    if (K <= 1024 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128K16P;
-    if (tiles(kCfgDma256x256K32P) >= kComputeUnits)
-        return streamk_pays(kCfgDma256x256K32P) ? kCfgDma256x256K32PSK : kCfgDma256x256K32P;
+    // 256 x 256 tiles: whole ones when they fill the rounds; stream-K over
+    // them only for K >= 3072 (6400 x 6400 x 4096: 2317 us against 2373 for
+    // stream-K over 128 x 128 tiles), below that the 128 x 128 choices
+    // (7369 x 2892 x 2379: 794 against 829; 3813 x 6105 x 766: 281 against
+    // 354).
+    if (tiles(kCfgDma256x256K32P) >= kComputeUnits) {
+        if (!streamk_pays(kCfgDma256x256K32P))
+            return kCfgDma256x256K32P;
+        if (K >= 3072)
+            return kCfgDma256x256K32PSK;
+    }
     const int64_t t128 = tiles(kCfgDma128x128K64P);
     if (t128 >= kComputeUnits) {
         if (!streamk_pays(kCfgDma128x128K64P)) {
@@ -1561,15 +1571,27 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
             // stores (6000 x 2000 x 1000: 185 us against 198).
             if (t128 >= 2 * kComputeUnits && K < 2048)
                 return kCfgDma128x128K16P;
+            // One or two rounds with a short K: a 64-deep panel ring has
+            // too few rounds to fill; 64 x 64 tiles balance better
+            // (5221 x 1201 x 233: 37.9 us against 50.5).
+            if (K < 512)
+                return kCfgDma64x64K32;
             return deep_ok ? kCfgDma128x128K64P : kCfgDma128x128K32S2;
         }
         // Stream-K's extra launch and split-tile passes pay off over a long
         // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
-        if (K >= 2048)
+        if (K >= 1024)
             return deep_ok ? kCfgDma128x128K64PSK : kCfgDma128x128K32W16SK;
         return kCfgDma64x64K32;
     }
-    if (deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits && unbalanced(kCfgDma64x64K32))
+    // At least three quarters of the CUs busy with 128 x 128 tiles: one
+    // round of them if 64 x 64 tiles would leave their last round mostly
+    // idle; with nine tenths busy and K >= 2048 also otherwise, the bigger
+    // tiles' efficiency outweighing the few idle CUs (2372 x 1619 x 7588,
+    // 247 tiles: 443 us against 504 for 64 x 64 tiles; 2200 x 1700 x 3000:
+    // 181 against 202).
+    if (deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits &&
+        (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 10 * t128 >= 9 * kComputeUnits)))
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them: K split
     // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
@@ -1602,7 +1624,12 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     if (K > 512 && t32 <= kComputeUnits)
         return K >= 2048 ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4;
     const int64_t last = t32 - (ceil_div(t32, kComputeUnits) - 1) * kComputeUnits;   // tiles in the last round
-    if (K > 512 && t32 <= 3 * kComputeUnits && 2 * last < kComputeUnits)
+    // (Past 320 tiles only with K >= 1100: below it the K-split groups'
+    // fold and stream-K's extra launch cost more than the idle CUs;
+    // 1600 x 1500 x 800: 53.7 us against 46.1 for 64 x 64 tiles; 1200 x 1200
+    // x 1000: 43.1 against 41.4; but 1100 x 1100 x 1100: 43.6 against 44.9.)
+    if (K > 512 && (K >= 1100 || t32 <= 5 * kComputeUnits / 4) && t32 <= 3 * kComputeUnits &&
+        2 * last < kComputeUnits)
         return kCfgDma64x64K32S4SK;
     if (K >= 2048 && t32 <= 2 * kComputeUnits)
         return kCfgDma64x64K16S8P;

@@ -168,7 +168,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_ksplit2 "), text
     rc, text = gb.gemm_f32_describe(-1, 3072, 3072, 3072, FAKE, 3072, FAKE, ldb, FAKE, 3072)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16_sk "), text
-    rc, text = gb.gemm_f32_describe(-1, 1100, 1100, 1100, FAKE, 1100, FAKE, ldb, FAKE, 1100)
+    rc, text = gb.gemm_f32_describe(-1, 1100, 1100, 1300, FAKE, 1300, FAKE, ldb, FAKE, 1100)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4_sk "), text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4 ") and "strip_rows=1" in text, text

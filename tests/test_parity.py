@@ -303,7 +303,7 @@ def test_graph_capture_replays_match_eager(dev):
         assert torch.equal(zout, torch.zeros_like(zout))
 
 
-GRAPH_PLANS = [((2048, 2048, 256), "dma_128x128x64_pipe "), ((4096, 4096, 128), "dma_128x128x16_pipe "),
+GRAPH_PLANS = [((2048, 2048, 512), "dma_128x128x64_pipe "), ((4096, 4096, 128), "dma_128x128x16_pipe "),
                ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((4096, 64, 2048), "dma_64x64x16_ksplit8_pipe ")]
 
 
