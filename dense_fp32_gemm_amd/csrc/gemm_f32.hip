@@ -1475,45 +1475,49 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
     return (c.bm - 1) * lda + c.bk < limit && (c.bk - 1) * ldb + c.bn < limit;
 }
 
-// Tile choice by shape, from the configuration sweep (sweep.py) on MI355X.
-// Output tiles are the unit of parallelism; the rule prefers the biggest
-// tiles of which there are enough for the 256 compute units:
-//  * K <= 512 with at least four 128 x 128 tiles per CU: 128 x 128, 4
+// Tile choice by shape, from configuration sweeps (sweep.py) on MI355X: the
+// workload shapes, square and mid-size shapes, and three sets of 40-44
+// random shapes (M, N log-uniform in 100..8192, K in 64..16384).  Output
+// tiles are the unit of parallelism; the rule prefers the biggest tiles of
+// which there are enough for the 256 compute units, and a stream-K twin
+// (all tiles' K-panels split evenly over one workgroup per CU) where the
+// last round of whole tiles would leave too many CUs idle:
+//  * K <= 1024 with at least four 128 x 128 tiles per CU: 128 x 128, 4
 //    pipelined waves on 16-deep panels, three workgroups per CU (short K:
 //    per-tile start-up and the C store weigh more than reuse; 8192 x 8192 x
 //    128: 143 us against 146.5 for the same tile unpipelined, 8192 x 8192 x
 //    512: 490 against 506);
 //  * at least one 256 x 256 tile per CU: 256 x 256 with 4 software-pipelined
-//    waves of 128 x 128, 32-deep panels (8192^3: 7.31 ms against 7.45 for
-//    16 waves of 64 x 64; 4096 x 4096 x 16384: 3.66 against 3.72);
+//    waves of 128 x 128, 32-deep panels, if they fill their rounds (8192^3:
+//    7.31 ms against 7.45 for 16 waves of 64 x 64; 4096 x 4096 x 16384: 3.66
+//    against 3.72); their stream-K twin for K >= 3072 if 128 x 128 tiles
+//    would not fill their rounds either (5000^3: 1832 us against 2381);
 //  * at least one 128 x 128 tile per CU: 128 x 128 with 4 pipelined waves
 //    of 64 x 64, 64-deep panels (2048^3: 125 us against 133 for 16 waves in
-//    two K-split groups); with two or more balanced rounds and K < 2048,
-//    16-deep panels and three workgroups per CU instead (4096 x 3072 x
-//    1024: 185 us against 193; but 4096 x 2048 x 2048: 250 against 247);
+//    two K-split groups); with two or more balanced rounds and K < 2048, or
+//    eight and more rounds, 16-deep panels and three workgroups per CU
+//    instead (4096 x 3072 x 1024: 185 us against 193; but 4096 x 2048 x
+//    2048: 250 against 247); their stream-K twin for K >= 1024 when the
+//    rounds are not filled (3072^3: 428 us against 455 for 64 x 64); below
+//    that, and for one or two rounds with K < 512, 64 x 64 tiles;
 //  * at least three quarters of the CUs busy with 128 x 128 tiles while
-//    64 x 64 tiles would leave the last round mostly idle: the pipelined
-//    128 x 128 tile too (1792^3: 110 us against 121 for 64 x 64);
+//    64 x 64 tiles would leave the last round mostly idle, or four fifths
+//    busy with K >= 2048: one round of the pipelined 128 x 128 tile (1792^3:
+//    110 us against 121 for 64 x 64);
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
 //    shapes): 64 x 64 with K split over wave groups inside the workgroup.
 //    For K >= 2048, 8 software-pipelined one-wave groups (16384 x 64 x 4096:
 //    72 us against 79 for 4 groups of 4 waves; 1024 x 1024 x 8192: 130
 //    against 149), below that 4 groups of 4 waves (1024^3: 25.4 us against
 //    26.3 for the 8 groups and 26.7 for 4 waves on 64-deep panels);
-//  * up to three rounds of 64 x 64 tiles with K > 512 and a last round under
-//    half full: stream-K over the 4-group K-split tile (1200 x 1200 x 4096:
-//    120 us against 149 for 64 x 64; 1536^3: 81 against 83; but 1280^3, a
-//    last round 56 % full: 53 against 51 for 64 x 64); otherwise two rounds
-//    with K >= 2048: the 8 pipelined groups (1300 x 1300 x 4096: 136 us
-//    against 149);
+//  * up to three rounds of 64 x 64 tiles with a last round under half full:
+//    stream-K over the 4-group K-split tile, past 320 tiles only with K >=
+//    1100 (1200 x 1200 x 4096: 120 us against 149 for 64 x 64; 1536^3: 81
+//    against 83; (1025, 1023, 1000): 37.2 against 42.3); otherwise two
+//    rounds with K >= 2048, or three with K >= 4096: the 8 pipelined groups
+//    (1300 x 1300 x 4096: 136 us against 149);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
-// When a tile count just above a multiple of 256 would leave most CUs idle
-// in the last round, a stream-K twin spreads all tiles' K-panels evenly over
-// one workgroup per CU (5000^3: 1832 us against 2381 for 256 x 256 tiles;
-// (1025, 1023, 1000) 37.2 us against 42.3 for 64 x 64); for 128 x 128 tiles
-// only with K >= 2048 (3072^3: 428 us against 455 for 64 x 64), since below
-// that 64 x 64 tiles do better ((2176, 2100, 1000): 92 us).
 // Below the largest tile the choices use 32- or 64-deep K-panels: those
 // tiles give each wave few MFMAs per panel, so fewer, deeper panels cut the
 // per-panel barrier, wait and LDS-latency cost (64-deep: +3 to +5 % at 1280^3
@@ -1553,23 +1557,26 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     if (K <= 1024 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128K16P;
     // 256 x 256 tiles: whole ones when they fill the rounds; stream-K over
-    // them only for K >= 3072 (6400 x 6400 x 4096: 2317 us against 2373 for
-    // stream-K over 128 x 128 tiles), below that the 128 x 128 choices
+    // them only for K >= 3072 and when 128 x 128 tiles would not fill their
+    // rounds either (6400 x 6400 x 4096: 2317 us against 2373 for stream-K
+    // over 128 x 128 tiles; but 6478 x 5640 x 3472, 2295 of 2304 128 x 128
+    // slots used: 1796 against 1909); otherwise the 128 x 128 choices
     // (7369 x 2892 x 2379: 794 against 829; 3813 x 6105 x 766: 281 against
     // 354).
     if (tiles(kCfgDma256x256K32P) >= kComputeUnits) {
         if (!streamk_pays(kCfgDma256x256K32P))
             return kCfgDma256x256K32P;
-        if (K >= 3072)
+        if (K >= 3072 && streamk_pays(kCfgDma128x128K64P))
             return kCfgDma256x256K32PSK;
     }
     const int64_t t128 = tiles(kCfgDma128x128K64P);
     if (t128 >= kComputeUnits) {
         if (!streamk_pays(kCfgDma128x128K64P)) {
-            // Two or more rounds with K < 2048: three resident workgroups of
-            // the 16-deep pipelined tile overlap each other's start-up and
-            // stores (6000 x 2000 x 1000: 185 us against 198).
-            if (t128 >= 2 * kComputeUnits && K < 2048)
+            // Two or more rounds with K < 2048, or eight and more with any K:
+            // three resident workgroups of the 16-deep pipelined tile overlap
+            // each other's start-up and stores (6000 x 2000 x 1000: 185 us
+            // against 198; 6478 x 5640 x 3472: 1796 against 1856).
+            if (t128 >= 2 * kComputeUnits && (K < 2048 || t128 >= 8 * kComputeUnits))
                 return kCfgDma128x128K16P;
             // One or two rounds with a short K: a 64-deep panel ring has
             // too few rounds to fill; 64 x 64 tiles balance better
@@ -1586,12 +1593,12 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     }
     // At least three quarters of the CUs busy with 128 x 128 tiles: one
     // round of them if 64 x 64 tiles would leave their last round mostly
-    // idle; with nine tenths busy and K >= 2048 also otherwise, the bigger
-    // tiles' efficiency outweighing the few idle CUs (2372 x 1619 x 7588,
-    // 247 tiles: 443 us against 504 for 64 x 64 tiles; 2200 x 1700 x 3000:
-    // 181 against 202).
+    // idle; with four fifths busy and K >= 2048 also otherwise, the bigger
+    // tiles' efficiency outweighing the idle CUs (2372 x 1619 x 7588, 247
+    // tiles: 443 us against 504 for 64 x 64 tiles; 1746 x 1863 x 3494, 210:
+    // 211 against 235; but 3072 x 1024 x 2048, 192: 126 against 109).
     if (deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits &&
-        (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 10 * t128 >= 9 * kComputeUnits)))
+        (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * kComputeUnits)))
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them: K split
     // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
