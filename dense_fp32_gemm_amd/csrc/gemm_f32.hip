@@ -1497,9 +1497,10 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    two K-split groups); with two or more balanced rounds and K < 2048, or
 //    eight and more rounds, 16-deep panels and three workgroups per CU
 //    instead (4096 x 3072 x 1024: 185 us against 193; but 4096 x 2048 x
-//    2048: 250 against 247); their stream-K twin for K >= 1024 when the
-//    rounds are not filled (3072^3: 428 us against 455 for 64 x 64); below
-//    that, and for one or two rounds with K < 512, 64 x 64 tiles;
+//    2048: 250 against 247); their stream-K twin when the rounds are not
+//    filled, for K >= 2048 or K >= 1024 with two or more tiles per CU
+//    (3072^3: 428 us against 455 for 64 x 64); otherwise, and for one or two
+//    rounds with K < 512, 64 x 64 tiles;
 //  * at least three quarters of the CUs busy with 128 x 128 tiles while
 //    64 x 64 tiles would leave the last round mostly idle, or four fifths
 //    busy with K >= 2048: one round of the pipelined 128 x 128 tile (1792^3:
@@ -1586,8 +1587,11 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
             return deep_ok ? kCfgDma128x128K64P : kCfgDma128x128K32S2;
         }
         // Stream-K's extra launch and split-tile passes pay off over a long
-        // K; otherwise four or more 64 x 64 tiles per CU balance well enough.
-        if (K >= 1024)
+        // K, from K = 1024 on with two or more tiles per CU; otherwise four
+        // or more 64 x 64 tiles per CU balance well enough (2200 x 2200 x
+        // 1500, 324 tiles: 135 us against 148 for stream-K; 941 x 4305 x
+        // 1100, 272: 81 against 107).
+        if (K >= 2048 || (K >= 1024 && t128 >= 2 * kComputeUnits))
             return deep_ok ? kCfgDma128x128K64PSK : kCfgDma128x128K32W16SK;
         return kCfgDma64x64K32;
     }
