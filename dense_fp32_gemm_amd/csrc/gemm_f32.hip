@@ -1524,7 +1524,10 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 // per-panel barrier, wait and LDS-latency cost (64-deep: +3 to +5 % at 1280^3
 // and 2048 x 1024 x 1024, one or two 64 x 64 tiles per CU).  With deep_ok
 // false (64-deep panels too tall for 32-bit offsets at the caller's leading
-// dimensions) the 32-deep alternatives are chosen instead.  Problems with
+// dimensions) the 32-deep alternatives are chosen instead.  Where 128-wide
+// tiles would cover over a quarter more padded area than 64 x 64 tiles (a
+// side of at most 64, or of 129 to 192), only the 64 x 64 choices are
+// considered (64 x 32768 x 4096: 154 us against 244).  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
 int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_rows, int &strip_cols)
@@ -1555,7 +1558,15 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
         const int64_t t = tiles(c);
         return K >= 1024 ? 25 * t < 24 * ceil_div(t, kComputeUnits) * kComputeUnits : unbalanced(c);
     };
-    if (K <= 1024 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
+    // A side of at most 64 (or 129 to 192) leaves 128-wide tiles a half (a
+    // third) padding; once their padded area is over a quarter larger than
+    // that of 64 x 64 tiles, only the 64 x 64 choices below are taken
+    // (64 x 32768 x 4096: 154 us against 244 for 128 x 128 tiles; 192 x
+    // 16384 x 4096: 202 against 243; 64 x 65536 x 1024: 75 against 240 for
+    // 256 x 256).
+    auto padded = [&](int edge) { return int64_t(ceil_div(M, edge)) * ceil_div(N, edge) * edge * edge; };
+    const bool thin = 4 * padded(128) > 5 * padded(64);
+    if (!thin && K <= 1024 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
         return kCfgDma128x128K16P;
     // 256 x 256 tiles: whole ones when they fill the rounds; stream-K over
     // them only for K >= 3072 and when 128 x 128 tiles would not fill their
@@ -1564,14 +1575,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // slots used: 1796 against 1909); otherwise the 128 x 128 choices
     // (7369 x 2892 x 2379: 794 against 829; 3813 x 6105 x 766: 281 against
     // 354).
-    if (tiles(kCfgDma256x256K32P) >= kComputeUnits) {
+    if (!thin && tiles(kCfgDma256x256K32P) >= kComputeUnits) {
         if (!streamk_pays(kCfgDma256x256K32P))
             return kCfgDma256x256K32P;
         if (K >= 3072 && streamk_pays(kCfgDma128x128K64P))
             return kCfgDma256x256K32PSK;
     }
     const int64_t t128 = tiles(kCfgDma128x128K64P);
-    if (t128 >= kComputeUnits) {
+    if (!thin && t128 >= kComputeUnits) {
         if (!streamk_pays(kCfgDma128x128K64P)) {
             // Two or more rounds with K < 2048, or eight and more with any K:
             // three resident workgroups of the 16-deep pipelined tile overlap
@@ -1601,7 +1612,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // tiles' efficiency outweighing the idle CUs (2372 x 1619 x 7588, 247
     // tiles: 443 us against 504 for 64 x 64 tiles; 1746 x 1863 x 3494, 210:
     // 211 against 235; but 3072 x 1024 x 2048, 192: 126 against 109).
-    if (deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits &&
+    if (!thin && deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits &&
         (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * kComputeUnits)))
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them: K split

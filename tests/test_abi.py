@@ -213,6 +213,12 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # panels for K < 2048
     ((6000, 2000, 1000), "dma_128x128x16_pipe "), ((4096, 3072, 1024), "dma_128x128x16_pipe "),
     ((4096, 2048, 2048), "dma_128x128x64_pipe "),
+    # a side of at most 64 (or 129 to 192): 128-wide tiles would be mostly
+    # padding, so only the 64 x 64 choices; a side of 96 or 128 keeps them
+    ((64, 32768, 4096), "dma_64x64x16_ksplit8_pipe "), ((32768, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
+    ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x64 "),
+    ((64, 65536, 1024), "dma_64x128x32 "), ((65536, 64, 1024), "dma_128x64x32 "),
+    ((96, 32768, 4096), "dma_128x128x64_pipe "), ((128, 32768, 4096), "dma_128x128x64_pipe "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe "),
 ])
