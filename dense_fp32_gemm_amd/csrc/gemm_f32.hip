@@ -1511,7 +1511,7 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    72 us against 79 for 4 groups of 4 waves; 1024 x 1024 x 8192: 130
 //    against 149), below that 4 groups of 4 waves (1024^3: 25.4 us against
 //    26.3 for the 8 groups and 26.7 for 4 waves on 64-deep panels);
-//  * up to three rounds of 64 x 64 tiles with a last round under half full:
+//  * up to three rounds of 64 x 64 tiles with a last round at most half full:
 //    stream-K over the 4-group K-split tile, past 320 tiles only with K >=
 //    1100 (1200 x 1200 x 4096: 120 us against 149 for 64 x 64; 1536^3: 81
 //    against 83; (1025, 1023, 1000): 37.2 against 42.3); otherwise two
@@ -1617,7 +1617,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them: K split
     // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
-    // for K >= 2048, else 4 groups of 4 waves; a last round under half full:
+    // for K >= 2048, else 4 groups of 4 waves; a last round at most half full:
     // stream-K over the 4-group tile; two rounds otherwise, with K >= 2048:
     // the 8 pipelined groups.
     const int64_t t32 = tiles(kCfgDma64x64K32);
@@ -1650,8 +1650,11 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // fold and stream-K's extra launch cost more than the idle CUs;
     // 1600 x 1500 x 800: 53.7 us against 46.1 for 64 x 64 tiles; 1200 x 1200
     // x 1000: 43.1 against 41.4; but 1100 x 1100 x 1100: 43.6 against 44.9.)
+    // (A last round exactly half full too: 384 tiles, 64 x 24576 x 4096:
+    // 126 us against 139 for the 8 pipelined groups; 24576 x 64 x 8192: 249
+    // against 267.)
     if (K > 512 && (K >= 1100 || t32 <= 5 * kComputeUnits / 4) && t32 <= 3 * kComputeUnits &&
-        2 * last < kComputeUnits)
+        2 * last <= kComputeUnits)
         return kCfgDma64x64K32S4SK;
     if (K >= 2048 && t32 <= 2 * kComputeUnits)
         return kCfgDma64x64K16S8P;

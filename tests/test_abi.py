@@ -219,6 +219,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x64 "),
     ((64, 65536, 1024), "dma_64x128x32 "), ((65536, 64, 1024), "dma_128x64x32 "),
     ((96, 32768, 4096), "dma_128x128x64_pipe "), ((128, 32768, 4096), "dma_128x128x64_pipe "),
+    # a second round exactly half full (384 tiles): stream-K over the K split
+    ((64, 24576, 4096), "dma_64x64x32_ksplit4_sk "), ((128, 12288, 12000), "dma_64x64x32_ksplit4_sk "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe "),
 ])
