@@ -137,9 +137,9 @@ def cpu_baseline(M, N, K, budget_s=12.0):
         t0 = time.perf_counter()
         oracle.gemm(np.ascontiguousarray(A[:rows]), B)
         dt = time.perf_counter() - t0
-        if dt > budget_s / 4 or rows >= M:
+        if dt > budget_s / 2 or rows >= M:
             break
-        rows = min(M, int(rows * max(2.0, budget_s / 2 / max(dt, 1e-3))))
+        rows = min(M, int(rows * max(2.0, budget_s / max(dt, 1e-3))))
     cores = oracle.threads()
     # One core: the full 512^3 product (about 0.3 s), for comparison with
     # single-threaded CPU figures.
