@@ -117,7 +117,9 @@ def test_2048_quarter_step_bit_exact(dev):
 LARGE = [(8192, 8192, 8192), (8192, 8192, 128), (16384, 64, 4096),
          (64, 16384, 4096), (4096, 4096, 16384),
          # thin shapes where the rule keeps to 64-wide tiles
-         (64, 32768, 4096), (65536, 64, 1024), (192, 16384, 4096)]
+         (64, 32768, 4096), (65536, 64, 1024), (192, 16384, 4096),
+         # a half-full second round: stream-K over the K-split tile
+         (64, 24576, 4096)]
 
 
 @pytest.mark.parametrize("shape", LARGE, ids=lambda s: "x".join(map(str, s)))
