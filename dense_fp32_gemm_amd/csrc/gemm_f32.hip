@@ -1631,15 +1631,15 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // both take 44.8, at 3 x 2048 the strip is 10 % slower).
     const int64_t t_full = (M / 64) * ceil_div(N, 64);
     static_assert(std::is_same<Tile64x64K32S4, StripTile>::value, "the strip tile is the 4-group K-split tile");
-    if (K > 512 && K < kMaxStripK && M % 64 != 0 && (M % 64) * K <= 4096 && t_full <= kComputeUnits &&
-        t32 > kComputeUnits) {
+    if (K > 512 && K < kMaxStripK && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
+        t_full <= kComputeUnits && t32 > kComputeUnits) {
         strip_rows = M % 64;
         return kCfgDma64x64K32S4;
     }
     // The same for a last tile column of at most kMaxStripRows columns.
     const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
-    if (K > 512 && K < kMaxStripK && N % 64 != 0 && (N % 64) * K <= 4096 && t_full_n <= kComputeUnits &&
-        t32 > kComputeUnits) {
+    if (K > 512 && K < kMaxStripK && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
+        t_full_n <= kComputeUnits && t32 > kComputeUnits) {
         strip_cols = N % 64;
         return kCfgDma64x64K32S4;
     }
@@ -1735,6 +1735,10 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
+    // The strip kernel sums at most kMaxStripRows rows (columns); the rule
+    // never plans a wider strip.
+    if (strip > kMaxStripRows || strip_c > kMaxStripRows)
+        return GEMM_F32_ERR_CONFIG;
     const int64_t tm = strip ? (M - strip) / kConfigs[c].bm : ceil_div(M, kConfigs[c].bm);
     const int64_t tn = strip_c ? (N - strip_c) / kConfigs[c].bn : ceil_div(N, kConfigs[c].bn);
     if (tm * tn > INT32_MAX)

@@ -290,3 +290,25 @@ def test_traffic_records_key_on_code_not_comments(tmp_path):
     c = tmp_path / "c.hip"
     c.write_text("int f(int x)\n{\n    return x + 2;\n}\n")
     assert bench.code_digest(a) == bench.code_digest(b) != bench.code_digest(c)
+
+
+def test_strip_width_never_exceeds_four():
+    """The strip kernel sums 1-4 rows (columns).  Sweep shapes around one
+    round of 64 x 64 tiles, where strips are planned, over K from just past
+    512 to the strip limit: every planned strip is at most 4 wide, and a
+    remainder of 5-63 rows or columns is never a strip."""
+    seen = set()
+    for base_m, base_n in ((1024, 1000), (1000, 1024), (960, 1088), (1088, 960), (1024, 1024)):
+        for rem in range(0, 64):
+            for K in (513, 600, 700, 819, 820, 1000, 1023, 1024, 1365, 2047):
+                for M, N in ((base_m + rem, base_n), (base_m, base_n + rem)):
+                    rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
+                    assert rc == gb.GEMM_F32_OK, (M, N, K, text)
+                    m = re.search(r"strip_(rows|cols)=(\d+)", text)
+                    if m:
+                        width = int(m.group(2))
+                        assert 1 <= width <= 4, (M, N, K, text)
+                        assert width == (M % 64 if m.group(1) == "rows" else N % 64), (M, N, K, text)
+                        seen.add((m.group(1), width))
+    # the sweep does reach strips of every width on both sides
+    assert seen == {(side, w) for side in ("rows", "cols") for w in (1, 2, 3, 4)}, seen

@@ -512,6 +512,23 @@ def test_strips_bit_exact_and_padding_kept(dev, shape, strip):
     assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 5):]).all()
 
 
+# A remainder of 5-7 rows or columns with K just past 512: once planned as a
+# strip wider than the strip kernel sums (fixed), now a plain plan.
+WIDE_REMAINDER = [(1029, 1000, 600), (1030, 1000, 600), (1031, 1000, 513), (1000, 1031, 513)]
+
+
+@pytest.mark.parametrize("shape", WIDE_REMAINDER, ids=lambda s: "x".join(map(str, s)))
+def test_wide_remainders_bit_exact_and_padding_kept(dev, shape):
+    M, N, K = shape
+    rc, desc = gb.gemm_f32_describe(-1, M, N, K, 16, K, 16, N, 16, N + 3)
+    assert rc == gb.GEMM_F32_OK and "strip" not in desc, desc
+    A, B = operands("quarter", M, N, K)
+    got, full = gpu_gemm(A, B, -1, dev, pad=(0, 0, 3))
+    assert_bit_exact(got, oracle.gemm(A, B), f"{shape}")
+    body = full[:M * (N + 3)].reshape(M, N + 3)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 3):]).all()
+
+
 @pytest.mark.parametrize("shape", [(1026, 1001, 1001), (1001, 1026, 1001)], ids=["rows", "cols"])
 def test_strips_uniform_within_tolerance_and_deterministic(dev, shape):
     A, B = operands("uniform", *shape)
