@@ -66,13 +66,27 @@ def load() -> ctypes.CDLL:
     return _lib
 
 
+INT32_MIN, INT32_MAX = -(1 << 31), (1 << 31) - 1
+
+
+def _ints(**vals):
+    """Refuses values a C int cannot hold: ctypes would wrap them silently
+    (2^32 + 1000 becomes 1000), turning an oversized size or leading
+    dimension into a different, valid-looking one."""
+    for name, v in vals.items():
+        if not INT32_MIN <= int(v) <= INT32_MAX:
+            raise ValueError(f"{name} = {v} does not fit the C ABI's 32-bit int")
+
+
 # --- the C ABI, one function per exported symbol ---------------------------
 def gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
     """C := A . B on `stream`; A, B, C are device addresses (ints)."""
+    _ints(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return load().gemm_f32(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_f32_with_config(config, M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    _ints(config=config, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return load().gemm_f32_with_config(config, M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
@@ -101,11 +115,13 @@ def gemm_f32_config_info(config: int, occupancy: bool = False) -> dict:
 
 def gemm_f32_ws_size(M, N, K) -> int:
     """Workspace bytes the split-K plan for this shape needs (0: not split)."""
+    _ints(M=M, N=N, K=K)
     return load().gemm_f32_ws_size(M, N, K)
 
 
 def gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream=0) -> int:
     """C := A . B, split over K through `workspace` when the shape calls for it."""
+    _ints(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return load().gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream)
 
 
@@ -121,6 +137,7 @@ def gemm_f32_device_peak(device: int = 0) -> dict:
 
 def gemm_f32_describe(config, M, N, K, A, lda, B, ldb, C, ldc) -> tuple[int, str]:
     """(status, description) of what gemm_f32_with_config would enqueue."""
+    _ints(config=config, M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     buf = ctypes.create_string_buffer(256)
     rc = load().gemm_f32_describe(config, M, N, K, A, lda, B, ldb, C, ldc, buf, len(buf))
     return rc, buf.value.decode()
@@ -159,6 +176,7 @@ def matmul(A, B, out=None, config: int = -1, stream=None):
         raise ValueError("inner dimensions differ")
     lda = _row_major(A, M, K, "A")
     ldb = _row_major(B, K, N, "B")
+    _ints(M=M, N=N, K=K, lda=lda, ldb=ldb)
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=A.device)
     ldc = _row_major(out, M, N, "out")

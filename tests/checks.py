@@ -19,8 +19,9 @@ def within_tolerance(got, ref, atol=ATOL, rtol=RTOL):
     assert g.shape == r.shape
     if g.size == 0:
         return True, 0.0, -1
-    diff = np.abs(g - r)
-    ok = diff <= atol + rtol * np.abs(r)        # NaN -> False
+    with np.errstate(invalid="ignore"):         # inf - inf is NaN, and fails below
+        diff = np.abs(g - r)
+        ok = diff <= atol + rtol * np.abs(r)    # NaN -> False
     ok &= np.isfinite(g)
     worst = int(np.argmax(np.where(np.isnan(diff), np.inf, diff)))
     return bool(ok.all()), float(diff[worst]), worst

@@ -312,3 +312,23 @@ def test_strip_width_never_exceeds_four():
                         seen.add((m.group(1), width))
     # the sweep does reach strips of every width on both sides
     assert seen == {(side, w) for side in ("rows", "cols") for w in (1, 2, 3, 4)}, seen
+
+
+def test_sizes_beyond_a_c_int_are_refused_before_the_call():
+    """ctypes would wrap 2^32 + 1000 to 1000; the binding raises instead."""
+    big = (1 << 32) + 1000
+    with pytest.raises(ValueError):
+        gb.gemm_f32(big, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0)
+    with pytest.raises(ValueError):
+        gb.gemm_f32(4, 4, 4, FAKE, big, FAKE, 4, FAKE, 4, 0)
+    with pytest.raises(ValueError):
+        gb.gemm_f32_with_config(-1, 4, 4, 4, FAKE, 4, FAKE, 4, FAKE, 1 << 31, 0)
+    with pytest.raises(ValueError):
+        gb.gemm_f32_ws(4, 4, big, FAKE, 4, FAKE, 4, FAKE, 4, FAKE, 1 << 20, 0)
+    with pytest.raises(ValueError):
+        gb.gemm_f32_ws_size(4, -(1 << 31) - 1, 4)
+    with pytest.raises(ValueError):
+        gb.gemm_f32_describe(-1, 4, 4, 4, FAKE, 4, FAKE, big, FAKE, 4)
+    # the extremes a C int holds still reach the library
+    assert gb.gemm_f32(-(1 << 31), 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_DIM
+    assert gb.gemm_f32(4, 4, 4, FAKE, (1 << 31) - 1, FAKE, 4, FAKE, 3, 0) == gb.GEMM_F32_ERR_LD
