@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+#include <atomic>
 #include <type_traits>
 #include <stdio.h>
 #include <string.h>
@@ -47,7 +48,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWaveSize = 64;
-constexpr int kXcdCount = 8;         // MI355X: 8 accelerator complex dies
 constexpr int64_t kMaxGrid = 1 << 20;  // workgroups per launch; larger jobs loop
 
 struct GemmArgs {
@@ -65,6 +65,7 @@ struct GemmArgs {
     int strip_cols;      // likewise columns N - strip_cols .. N-1, right of
                          // the grid, for the last tile column (not together
                          // with strip_rows)
+    int xcds;            // dies the device hands workgroups to round-robin
 };
 
 // Most rows a remainder strip may hold, and its largest K: the strip's rows
@@ -76,16 +77,16 @@ constexpr int kMaxStripK = 2048;
 // Tile scheduling
 // ---------------------------------------------------------------------------
 
-// Workgroups are handed to the 8 XCDs round-robin (workgroup w runs on XCD
-// w mod 8), and each XCD has its own L2.  Renumber so that each XCD receives a
-// contiguous range of logical tiles; neighbouring tiles share A rows and B
-// columns, so their panels are fetched once per L2.
-__device__ inline int xcd_contiguous(int w, int total)
+// Workgroups are handed to the XCDs round-robin (on a whole MI355X, workgroup
+// w runs on XCD w mod 8), and each XCD has its own L2.  Renumber so that each
+// XCD receives a contiguous range of logical tiles; neighbouring tiles share
+// A rows and B columns, so their panels are fetched once per L2.
+__device__ inline int xcd_contiguous(int w, int total, int xcds)
 {
-    const int per = total / kXcdCount;
-    const int rem = total % kXcdCount;
-    const int xcd = w % kXcdCount;
-    return xcd * per + (xcd < rem ? xcd : rem) + w / kXcdCount;
+    const int per = total / xcds;
+    const int rem = total % xcds;
+    const int xcd = w % xcds;
+    return xcd * per + (xcd < rem ? xcd : rem) + w / xcds;
 }
 
 // Logical tile id -> (tile row, tile column), walking groups of `group` tile
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 
     const int total = g.tiles_m * g.tiles_n;
     for (int w = blockIdx.x; w < total; w += gridDim.x) {
-        const int t = (int)gridDim.x == total ? xcd_contiguous(w, total) : w;
+        const int t = (int)gridDim.x == total ? xcd_contiguous(w, total, g.xcds) : w;
         int tm, tn;
         tile_coords(t, g.tiles_m, g.tiles_n, T::kGroup, tm, tn);
         const int m0 = tm * BM;
@@ -1103,7 +1104,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
              (int)((int64_t)(slice + 1) * ktiles / g.slices));
     } else if (SK) {
         int64_t lo, hi;
-        streamk_range(xcd_contiguous(blockIdx.x, gridDim.x), gridDim.x, (int64_t)total * ktiles, lo, hi);
+        streamk_range(xcd_contiguous(blockIdx.x, gridDim.x, g.xcds), gridDim.x, (int64_t)total * ktiles, lo, hi);
         while (lo < hi) {
             const int t = (int)(lo / ktiles);
             const int p0 = (int)(lo - (int64_t)t * ktiles);
@@ -1113,7 +1114,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         }
     } else {
         for (int w = blockIdx.x; w < total; w += gridDim.x)
-            work((int)gridDim.x == total ? xcd_contiguous(w, total) : w, 0, ktiles);
+            work((int)gridDim.x == total ? xcd_contiguous(w, total, g.xcds) : w, 0, ktiles);
     }
 }
 
@@ -1240,22 +1241,13 @@ __global__ __launch_bounds__(256) void fill_zero(float *C, int64_t ldc, int M, i
 // waves each owning a (BM/WAVES_M) x (BN/WAVES_N) block; optional K-split
 // groups, panel-ring depth, loader-wave count and the software-pipelined
 // round loop.
-using Tile256x256W16 = MfmaTile<256, 256, 16, 4, 4, 1, 2, 8, 8>;    // 16 waves of 64 x 64, 8 load
-using Tile128x128W16 = MfmaTile<128, 128, 16, 4, 4, 1, 2, 8, 8>;    // 16 waves of 32 x 32, 8 load
-using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;       // 4 waves of 64 x 64
-using Tile128x64 = MfmaTile<128, 64, 16, 2, 2>;         // 4 waves of 64 x 32
-using Tile64x128 = MfmaTile<64, 128, 16, 2, 2>;         // 4 waves of 32 x 64
-using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;           // 4 waves of 32 x 32
-using Tile64x64S4 = MfmaTile<64, 64, 16, 2, 2, 4>;      // 4 K-split groups of 4 waves
-using Tile128x128R3 = MfmaTile<128, 128, 16, 2, 2, 1, 3>;   // three-buffer panel ring
-using Tile64x64S4R3 = MfmaTile<64, 64, 16, 2, 2, 4, 3>;
-using Tile256x256K32W16 = MfmaTile<256, 256, 32, 4, 4, 1, 2, 8, 8>;  // 32-deep panels
-using Tile128x128K32W16 = MfmaTile<128, 128, 32, 4, 4, 1, 2, 8, 8>;
+using Tile128x128 = MfmaTile<128, 128, 16, 2, 2>;       // 4 waves of 64 x 64 (staged fallback)
+using Tile64x64 = MfmaTile<64, 64, 16, 2, 2>;           // 4 waves of 32 x 32 (staged fallback)
+using Tile128x128K32W16 = MfmaTile<128, 128, 32, 4, 4, 1, 2, 8, 8>;  // 16 waves of 32 x 32, 8 load
 using Tile64x64K32 = MfmaTile<64, 64, 32, 2, 2>;
-using Tile64x64K32S4 = MfmaTile<64, 64, 32, 2, 2, 4>;
+using Tile64x64K32S4 = MfmaTile<64, 64, 32, 2, 2, 4>;   // 4 K-split groups of 4 waves
 using Tile64x128K32 = MfmaTile<64, 128, 32, 2, 2>;
 using Tile128x64K32 = MfmaTile<128, 64, 32, 2, 2>;
-using Tile128x128K32 = MfmaTile<128, 128, 32, 2, 2>;
 using Tile64x64K64 = MfmaTile<64, 64, 64, 2, 2>;         // 64-deep panels
 // 2 K-split groups of 8 waves of 32 x 64, 4 of them loading
 using Tile128x128K32S2 = MfmaTile<128, 128, 32, 4, 2, 2, 2, 8, 4>;
@@ -1269,29 +1261,20 @@ using Tile64x64K16S8P = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
 // three workgroups per CU)
 using Tile128x128K16P = MfmaTile<128, 128, 16, 2, 2, 1, 2, 8, 0, 1>;
 
+// Every configuration is one the shape rule (select_config) picks for some
+// shapes, or the register-staged fallback for rows too long for 32-bit
+// panel offsets; each also runs under gemm_f32_with_config for tests and
+// sweeps.
 enum ConfigId {
     kCfgValu64 = 0,
-    kCfgDma256x256W16,
-    kCfgDma128x128W16,
-    kCfgDma128x128,
-    kCfgDma128x64,
-    kCfgDma64x128,
-    kCfgDma64x64,
-    kCfgDma64x64S4,
-    kCfgDma128x128R3,
-    kCfgDma64x64S4R3,
     kCfgStaged128x128,
     kCfgStaged64x64,
-    kCfgDma256x256K32W16,
-    kCfgDma128x128K32W16,
     kCfgDma64x64K32,
     kCfgDma64x64K32S4,
     kCfgDma64x128K32,
     kCfgDma128x64K32,
-    kCfgDma128x128K32,
     kCfgDma64x64K32SK,
     kCfgDma128x128K32W16SK,
-    kCfgDma256x256K32W16SK,
     kCfgDma64x64K64,
     kCfgDma64x64K64SK,
     kCfgDma128x128K32S2,
@@ -1300,7 +1283,6 @@ enum ConfigId {
     kCfgDma128x128K64P,
     kCfgDma128x128K64PSK,
     kCfgDma64x64K16S8P,
-    kCfgDma64x64K16S8PSK,
     kCfgDma64x64K32S4SK,
     kCfgDma128x128K16P,
     kNumConfigs
@@ -1428,27 +1410,14 @@ constexpr ConfigInfo config_streamk(const char *name)
 // Indexed by ConfigId.
 const ConfigInfo kConfigs[kNumConfigs] = {
     {"valu_64x64", kValuTile, kValuTile, kValuBK, kValuThreads, false, &launch_valu, &occupancy_valu, false, nullptr},
-    config_dma<Tile256x256W16>("dma_256x256x16_w16"),
-    config_dma<Tile128x128W16>("dma_128x128x16_w16"),
-    config_dma<Tile128x128>("dma_128x128x16"),
-    config_dma<Tile128x64>("dma_128x64x16"),
-    config_dma<Tile64x128>("dma_64x128x16"),
-    config_dma<Tile64x64>("dma_64x64x16"),
-    config_dma<Tile64x64S4>("dma_64x64x16_ksplit4"),
-    config_dma<Tile128x128R3>("dma_128x128x16_ring3"),
-    config_dma<Tile64x64S4R3>("dma_64x64x16_ksplit4_ring3"),
     config_staged<Tile128x128>("staged_128x128x16"),
     config_staged<Tile64x64>("staged_64x64x16"),
-    config_dma<Tile256x256K32W16>("dma_256x256x32_w16"),
-    config_dma<Tile128x128K32W16>("dma_128x128x32_w16"),
     config_dma<Tile64x64K32, true>("dma_64x64x32"),
     config_dma<Tile64x64K32S4>("dma_64x64x32_ksplit4"),
     config_dma<Tile64x128K32, true>("dma_64x128x32"),
     config_dma<Tile128x64K32, true>("dma_128x64x32"),
-    config_dma<Tile128x128K32>("dma_128x128x32"),
     config_streamk<Tile64x64K32, true>("dma_64x64x32_sk"),
     config_streamk<Tile128x128K32W16>("dma_128x128x32_w16_sk"),
-    config_streamk<Tile256x256K32W16>("dma_256x256x32_w16_sk"),
     config_dma<Tile64x64K64>("dma_64x64x64"),
     config_streamk<Tile64x64K64>("dma_64x64x64_sk"),
     config_dma<Tile128x128K32S2>("dma_128x128x32_ksplit2"),
@@ -1457,14 +1426,44 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile128x128K64P, true>("dma_128x128x64_pipe"),
     config_streamk<Tile128x128K64P, true>("dma_128x128x64_pipe_sk"),
     config_dma<Tile64x64K16S8P, true>("dma_64x64x16_ksplit8_pipe"),
-    config_streamk<Tile64x64K16S8P, true>("dma_64x64x16_ksplit8_pipe_sk"),
     config_streamk<Tile64x64K32S4>("dma_64x64x32_ksplit4_sk"),
     config_dma<Tile128x128K16P, true>("dma_128x128x16_pipe"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int64_t kComputeUnits = 256;   // MI355X
+// The device the work runs on, read once per device: its compute units
+// (the unit the shape rule balances tiles over, and stream-K's worker count)
+// and the dies (XCDs, 32 compute units each on MI355X) workgroups are dealt
+// to round-robin.  A whole MI355X has 256 and 8; a partitioned one fewer.
+// Without a usable device (plans described on a host without a GPU) the
+// whole MI355X is assumed.
+struct Machine {
+    int64_t cus;
+    int xcds;
+};
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];   // 0: not read yet
+
+Machine machine()
+{
+    constexpr int kDefaultCus = 256, kCusPerXcd = 32;
+    int dev = -1, cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        cu = kDefaultCus;
+    } else {
+        cu = g_device_cus[dev].load(std::memory_order_relaxed);
+        if (cu == 0) {
+            if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0) {
+                (void)hipGetLastError();
+                cu = kDefaultCus;
+            }
+            g_device_cus[dev].store(cu, std::memory_order_relaxed);
+        }
+    }
+    return {cu, cu % kCusPerXcd == 0 ? cu / kCusPerXcd : 1};
+}
 
 // The direct-to-LDS kernels address each panel with 32-bit buffer offsets
 // from its corner: the farthest in-range element of an A panel is
@@ -1530,14 +1529,14 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 // considered (64 x 32768 x 4096: 154 us against 244).  Problems with
 // fewer than 16 rows or columns use the vector-FMA kernel, where a 32-wide
 // matrix-core block would be mostly padding.
-int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_rows, int &strip_cols)
+int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, int &strip_rows, int &strip_cols)
 {
     strip_rows = strip_cols = 0;
     if (M < 16 || N < 16)
         return kCfgValu64;
     auto tiles = [&](int c) { return ceil_div(M, kConfigs[c].bm) * ceil_div(N, kConfigs[c].bn); };
     if (!dma_ok) {
-        if (tiles(kCfgStaged128x128) >= 4 * kComputeUnits)
+        if (tiles(kCfgStaged128x128) >= 4 * CU)
             return kCfgStaged128x128;
         return kCfgStaged64x64;
     }
@@ -1545,7 +1544,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // leaves more than a fifth of the CU-rounds idle when this is true:
     auto unbalanced = [&](int c) {
         const int64_t t = tiles(c);
-        return 5 * t < 4 * ceil_div(t, kComputeUnits) * kComputeUnits;
+        return 5 * t < 4 * ceil_div(t, CU) * CU;
     };
     // Whether stream-K's even split beats whole tiles: over a long K its
     // extra launch and split tiles cost about 3 %, so it pays once the last
@@ -1556,7 +1555,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // 4096, 98 %: 730 against 719); below K = 1024 only past a fifth.
     auto streamk_pays = [&](int c) {
         const int64_t t = tiles(c);
-        return K >= 1024 ? 25 * t < 24 * ceil_div(t, kComputeUnits) * kComputeUnits : unbalanced(c);
+        return K >= 1024 ? 25 * t < 24 * ceil_div(t, CU) * CU : unbalanced(c);
     };
     // A side of at most 64 (or 129 to 192) leaves 128-wide tiles a half (a
     // third) padding; once their padded area is over a quarter larger than
@@ -1566,7 +1565,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // 256 x 256).
     auto padded = [&](int edge) { return int64_t(ceil_div(M, edge)) * ceil_div(N, edge) * edge * edge; };
     const bool thin = 4 * padded(128) > 5 * padded(64);
-    if (!thin && K <= 1024 && tiles(kCfgDma128x128) >= 4 * kComputeUnits)
+    if (!thin && K <= 1024 && tiles(kCfgDma128x128K16P) >= 4 * CU)
         return kCfgDma128x128K16P;
     // 256 x 256 tiles: whole ones when they fill the rounds; stream-K over
     // them only for K >= 3072 and when 128 x 128 tiles would not fill their
@@ -1575,20 +1574,20 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // slots used: 1796 against 1909); otherwise the 128 x 128 choices
     // (7369 x 2892 x 2379: 794 against 829; 3813 x 6105 x 766: 281 against
     // 354).
-    if (!thin && tiles(kCfgDma256x256K32P) >= kComputeUnits) {
+    if (!thin && tiles(kCfgDma256x256K32P) >= CU) {
         if (!streamk_pays(kCfgDma256x256K32P))
             return kCfgDma256x256K32P;
         if (K >= 3072 && streamk_pays(kCfgDma128x128K64P))
             return kCfgDma256x256K32PSK;
     }
     const int64_t t128 = tiles(kCfgDma128x128K64P);
-    if (!thin && t128 >= kComputeUnits) {
+    if (!thin && t128 >= CU) {
         if (!streamk_pays(kCfgDma128x128K64P)) {
             // Two or more rounds with K < 2048, or eight and more with any K:
             // three resident workgroups of the 16-deep pipelined tile overlap
             // each other's start-up and stores (6000 x 2000 x 1000: 185 us
             // against 198; 6478 x 5640 x 3472: 1796 against 1856).
-            if (t128 >= 2 * kComputeUnits && (K < 2048 || t128 >= 8 * kComputeUnits))
+            if (t128 >= 2 * CU && (K < 2048 || t128 >= 8 * CU))
                 return kCfgDma128x128K16P;
             // One or two rounds with a short K: a 64-deep panel ring has
             // too few rounds to fill; 64 x 64 tiles balance better
@@ -1602,7 +1601,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
         // or more 64 x 64 tiles per CU balance well enough (2200 x 2200 x
         // 1500, 324 tiles: 135 us against 148 for stream-K; 941 x 4305 x
         // 1100, 272: 81 against 107).
-        if (K >= 2048 || (K >= 1024 && t128 >= 2 * kComputeUnits))
+        if (K >= 2048 || (K >= 1024 && t128 >= 2 * CU))
             return deep_ok ? kCfgDma128x128K64PSK : kCfgDma128x128K32W16SK;
         return kCfgDma64x64K32;
     }
@@ -1612,8 +1611,8 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // tiles' efficiency outweighing the idle CUs (2372 x 1619 x 7588, 247
     // tiles: 443 us against 504 for 64 x 64 tiles; 1746 x 1863 x 3494, 210:
     // 211 against 235; but 3072 x 1024 x 2048, 192: 126 against 109).
-    if (!thin && deep_ok && K > 512 && 4 * t128 >= 3 * kComputeUnits &&
-        (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * kComputeUnits)))
+    if (!thin && deep_ok && K > 512 && 4 * t128 >= 3 * CU &&
+        (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * CU)))
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them: K split
     // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
@@ -1632,20 +1631,20 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     const int64_t t_full = (M / 64) * ceil_div(N, 64);
     static_assert(std::is_same<Tile64x64K32S4, StripTile>::value, "the strip tile is the 4-group K-split tile");
     if (K > 512 && K < kMaxStripK && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
-        t_full <= kComputeUnits && t32 > kComputeUnits) {
+        t_full <= CU && t32 > CU) {
         strip_rows = M % 64;
         return kCfgDma64x64K32S4;
     }
     // The same for a last tile column of at most kMaxStripRows columns.
     const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
     if (K > 512 && K < kMaxStripK && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
-        t_full_n <= kComputeUnits && t32 > kComputeUnits) {
+        t_full_n <= CU && t32 > CU) {
         strip_cols = N % 64;
         return kCfgDma64x64K32S4;
     }
-    if (K > 512 && t32 <= kComputeUnits)
+    if (K > 512 && t32 <= CU)
         return K >= 2048 ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4;
-    const int64_t last = t32 - (ceil_div(t32, kComputeUnits) - 1) * kComputeUnits;   // tiles in the last round
+    const int64_t last = t32 - (ceil_div(t32, CU) - 1) * CU;   // tiles in the last round
     // (Past 320 tiles only with K >= 1100: below it the K-split groups'
     // fold and stream-K's extra launch cost more than the idle CUs;
     // 1600 x 1500 x 800: 53.7 us against 46.1 for 64 x 64 tiles; 1200 x 1200
@@ -1653,19 +1652,19 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // (A last round exactly half full too: 384 tiles, 64 x 24576 x 4096:
     // 126 us against 139 for the 8 pipelined groups; 24576 x 64 x 8192: 249
     // against 267.)
-    if (K > 512 && (K >= 1100 || t32 <= 5 * kComputeUnits / 4) && t32 <= 3 * kComputeUnits &&
-        2 * last <= kComputeUnits)
+    if (K > 512 && (K >= 1100 || t32 <= 5 * CU / 4) && t32 <= 3 * CU &&
+        2 * last <= CU)
         return kCfgDma64x64K32S4SK;
-    if (K >= 2048 && t32 <= 2 * kComputeUnits)
+    if (K >= 2048 && t32 <= 2 * CU)
         return kCfgDma64x64K16S8P;
     // Three rounds with a fuller last one still favour the 8 pipelined
     // groups once K is long (5932 x 460 x 4096: 200 us against 213 for
     // 64 x 64 tiles of 4 waves; x 8192: 378 against 419; x 2048: 112
     // against 110).
-    if (K >= 4096 && t32 <= 3 * kComputeUnits)
+    if (K >= 4096 && t32 <= 3 * CU)
         return kCfgDma64x64K16S8P;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
-    if (tiles(wide) >= 2 * kComputeUnits)
+    if (tiles(wide) >= 2 * CU)
         return wide;
     // 64 x 64 tiles.  Up to two per CU, the one or two 4-wave workgroups
     // leave each SIMD one or two waves, and 64-deep panels halve the
@@ -1675,9 +1674,9 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int &strip_row
     // Barely more than one tile per CU: stream-K, so the few extra tiles do
     // not double the time.
     const int64_t t64 = tiles(kCfgDma64x64K64);
-    if (t64 > kComputeUnits && 4 * t64 <= 5 * kComputeUnits)
+    if (t64 > CU && 4 * t64 <= 5 * CU)
         return deep_ok ? kCfgDma64x64K64SK : kCfgDma64x64K32SK;
-    if (t64 <= 2 * kComputeUnits)
+    if (t64 <= 2 * CU)
         return deep_ok ? kCfgDma64x64K64 : kCfgDma64x64K32;
     return kCfgDma64x64K32;
 }
@@ -1692,6 +1691,9 @@ struct Plan {
     int grid;
     int strip_rows;      // rows below the tile grid, computed as a strip
     int strip_cols;      // columns right of it, computed as a strip
+    int xcds;            // the device's dies (tile order)
+    bool shares_tiles;   // stream-K: some tiles are summed in C by two
+                         // workgroups with atomic adds
 };
 
 // Validates the arguments (sizes, leading dimensions, configuration index,
@@ -1711,6 +1713,8 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     plan->wb_c = false;
     plan->tiles_m = plan->tiles_n = plan->grid = 0;
     plan->strip_rows = plan->strip_cols = 0;
+    plan->xcds = 1;
+    plan->shares_tiles = false;
     if (M == 0 || N == 0)
         return GEMM_F32_OK;
     if (C == nullptr || (K > 0 && (A == nullptr || B == nullptr)))
@@ -1723,15 +1727,17 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     }
     int c = config;
     int strip = 0, strip_c = 0;
+    const Machine mach = machine();
+    plan->xcds = mach.xcds;
     if (c < 0) {
         // The rule's direct-to-LDS choice; if its panels are too tall or deep
         // for 32-bit offsets at these leading dimensions, its choice among
         // 32-deep panels, and failing that the register-staged kernel.
-        c = select_config(M, N, K, true, true, strip, strip_c);
+        c = select_config(M, N, K, true, true, mach.cus, strip, strip_c);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, true, false, strip, strip_c);
+            c = select_config(M, N, K, true, false, mach.cus, strip, strip_c);
         if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb))
-            c = select_config(M, N, K, false, false, strip, strip_c);
+            c = select_config(M, N, K, false, false, mach.cus, strip, strip_c);
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
@@ -1748,9 +1754,16 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     plan->strip_cols = strip_c;
     plan->tiles_m = (int)tm;
     plan->tiles_n = (int)tn;
-    if (kConfigs[c].streamk)
-        plan->grid = (int)(tm * tn < kComputeUnits ? tm * tn : kComputeUnits);
-    else
+    if (kConfigs[c].streamk) {
+        plan->grid = (int)(tm * tn < mach.cus ? tm * tn : mach.cus);
+        // A tile is shared when a worker's range starts inside it (the
+        // workers' ranges as streamk_range cuts them).
+        const int64_t ktiles = ceil_div(K, kConfigs[c].bk), iters = tm * tn * ktiles;
+        for (int b = 1; b < plan->grid && !plan->shares_tiles; ++b) {
+            const int64_t lo = iters / plan->grid * b + iters % plan->grid * b / plan->grid;
+            plan->shares_tiles = lo % ktiles != 0;
+        }
+    } else
         plan->grid = (int)(tm * tn < kMaxGrid ? tm * tn : kMaxGrid);
     plan->wb_c = kConfigs[c].launch_wb != nullptr && !strip && !strip_c &&
                  !(aligned16(C) && ldc % 4 == 0) && (int64_t)M * N >= kWriteBackFromElems;
@@ -1798,6 +1811,7 @@ int run(int config, int M, int N, int K, const float *A, int lda, const float *B
     g.slab = 0;
     g.strip_rows = p.strip_rows;
     g.strip_cols = p.strip_cols;
+    g.xcds = p.xcds;
     // A plan with a remainder strip runs the strip tile's strip kernel (the
     // rule pairs strips with that tile only).
     const hipError_t err = p.strip_rows > 0 || p.strip_cols > 0
@@ -1822,10 +1836,11 @@ int splitk_slices(int M, int N, int K)
 {
     if (M < 16 || N < 16 || K <= 0)
         return 1;
+    const int64_t cus = machine().cus;
     const int64_t t = ceil_div(M, TileSplitK::BM) * ceil_div(N, TileSplitK::BN);
-    if (2 * t > kComputeUnits)
+    if (2 * t > cus)
         return 1;
-    int64_t slices = kComputeUnits / t;
+    int64_t slices = cus / t;
     const int64_t by_depth = ceil_div(K, TileSplitK::BK) / kSplitKMinPanels;
     if (by_depth < slices)
         slices = by_depth;
@@ -1872,6 +1887,7 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     g.slices = slices;
     g.slab = (int64_t)M * N;
     g.strip_rows = g.strip_cols = 0;
+    g.xcds = p.xcds;
     const int grid = g.tiles_m * g.tiles_n * slices;
     hipError_t err = pipe ? LaunchDma<Tile64x64K16S8P, false, true>::run(g, true, true, grid, stream)
                           : LaunchDma<TileSplitK, false, true>::run(g, true, true, grid, stream);
@@ -1974,6 +1990,9 @@ int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
             snprintf(buf + n, (size_t)(buflen - n), " strip_cols=%d", p.strip_cols);
         else if (p.wb_c && n >= 0 && n < buflen)
             snprintf(buf + n, (size_t)(buflen - n), " c_store=write_back");
+        const int used = (int)strlen(buf);
+        if (p.shares_tiles && used + 1 < buflen)
+            snprintf(buf + used, (size_t)(buflen - used), " c_accumulate=atomic_add");
     }
     return rc;
 }

@@ -31,9 +31,13 @@
  * splits the K range of some output tiles between two workgroups, first
  * clears those tiles and then adds both partial sums into C with hardware
  * atomic float adds.  Exactly two addends on +0.0 commute, so the result is
- * the same whichever lands first: every configuration is deterministic.  The
- * library allocates no device memory and keeps no state between calls; it is
- * safe to call from several host threads.
+ * the same whichever lands first: every configuration is deterministic
+ * (gemm_f32_describe() marks such plans).  The library allocates no device
+ * memory.  Its only state is each device's compute-unit count, read once
+ * (hipDeviceGetAttribute) on the first call that plans work for the current
+ * device and used to size the tile rounds; without a usable device the
+ * 256 compute units of a whole MI355X are assumed.  It is safe to call from
+ * several host threads.
  *
  * Asynchrony: every call only enqueues work on `stream` (a hipStream_t; 0 is
  * the null stream) and returns.  Errors detected while the kernels run are
@@ -152,7 +156,10 @@ GEMM_F32_API int gemm_f32_config_info(int config, int *bm, int *bn, int *bk,
  * " strip_rows=R" or " strip_cols=C"; when C has at least 2^23 elements and
  * rows that are not 16-byte aligned (C's address or ldc * 4 not a multiple
  * of 16) and the configuration has such a variant, " c_store=write_back"
- * (C written with ordinary rather than streaming stores).
+ * (C written with ordinary rather than streaming stores); last, when a
+ * stream-K plan splits some tiles' K range between two workgroups, which
+ * then add their partial sums into C with atomic adds (C must be ordinary
+ * device memory), " c_accumulate=atomic_add".
  * Pointers are only inspected for alignment, never dereferenced.  Returns the
  * status the call would return for the same arguments.
  */

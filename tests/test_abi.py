@@ -120,7 +120,7 @@ def test_describe():
 
 WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
               "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
-              "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe", "dma_64x64x16_ksplit8_pipe_sk",
+              "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe",
               "dma_128x128x16_pipe"]
 
 
@@ -332,3 +332,25 @@ def test_sizes_beyond_a_c_int_are_refused_before_the_call():
     # the extremes a C int holds still reach the library
     assert gb.gemm_f32(-(1 << 31), 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_DIM
     assert gb.gemm_f32(4, 4, 4, FAKE, (1 << 31) - 1, FAKE, 4, FAKE, 3, 0) == gb.GEMM_F32_ERR_LD
+
+
+def test_describe_names_plans_that_add_into_c():
+    """Stream-K plans whose workers split a tile's K-panels sum that tile in C
+    with atomic adds (C must be ordinary device memory); describe says so."""
+    rc, text = gb.gemm_f32_describe(-1, 1025, 1025, 1000, FAKE, 1000, FAKE, 1025, FAKE, 1025)
+    assert rc == gb.GEMM_F32_OK and "_sk " in text and text.endswith(" c_accumulate=atomic_add"), text
+    sk = gb.config_names().index("dma_64x64x64_sk")
+    # fewer tiles than workers: one worker per tile, nothing shared
+    rc, text = gb.gemm_f32_describe(sk, 300, 300, 1000, FAKE, 1000, FAKE, 300, FAKE, 300)
+    assert "grid=25 " in text and "atomic" not in text, text
+    # 512 tiles, 64 panels each, over 256 workers: every range is two whole tiles
+    rc, text = gb.gemm_f32_describe(sk, 1024, 2048, 4096, FAKE, 4096, FAKE, 2048, FAKE, 2048)
+    assert "tiles=16x32 grid=256 " in text and "atomic" not in text, text
+    for shape in [(8192, 8192, 8192), (2048, 2048, 2048), (1000, 1000, 1000), (1025, 1023, 1000)]:
+        M, N, K = shape
+        rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
+        assert "atomic" not in text, text
+    # with the write-back twin both markers appear
+    wb_sk = gb.config_names().index("dma_64x64x32_sk")
+    rc, text = gb.gemm_f32_describe(wb_sk, 2049, 4097, 40, FAKE, 40, FAKE, 4097, FAKE, 4097)
+    assert text.endswith(" c_store=write_back c_accumulate=atomic_add"), text

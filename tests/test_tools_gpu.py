@@ -41,3 +41,11 @@ def test_device_peak(cuda):
     assert p["compute_units"] == cuda.cuda.get_device_properties(0).multi_processor_count
     assert 1_000_000 <= p["clock_khz"] <= 4_000_000
     assert p["tflops"] == pytest.approx(p["compute_units"] * 256 * p["clock_khz"] * 1e3 / 1e12)
+
+
+def test_plans_are_sized_from_the_device(cuda):
+    """Stream-K runs one worker per compute unit of the current device."""
+    cus = cuda.cuda.get_device_properties(0).multi_processor_count
+    fake = 0x100000
+    rc, text = gb.gemm_f32_describe(-1, 1025, 1025, 1000, fake, 1000, fake, 1025, fake, 1025)
+    assert rc == gb.GEMM_F32_OK and f" grid={cus} " in text, text
