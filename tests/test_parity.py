@@ -133,6 +133,27 @@ def test_large_sampled(dev, shape):
     assert np.isfinite(got).all()
 
 
+# The scaling report's sizes (n = 128 ... 8192, doubling), each checked in
+# full: all n^2 outputs of gemm_f32 on quarter-step operands against the
+# oracle, bit for bit, with the configuration the report times.
+REPORT_SIZES = [128 << i for i in range(7)]
+
+
+@pytest.mark.parametrize("n", REPORT_SIZES)
+def test_report_sizes_full_bit_exact(dev, n):
+    from dense_fp32_gemm_amd import report
+    A, B = inputs.quarter_step(n, n, n)
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.full((n, n), float("nan"), dtype=torch.float32, device=dev)
+    say(f"report size n={n}: gemm_f32 on quarter-step operands, full oracle")
+    assert report._gemm(-1, dA, dB, dC, torch.cuda.current_stream()) == gb.GEMM_F32_OK
+    torch.cuda.synchronize()
+    got = dC.cpu().numpy()
+    del dA, dB, dC
+    assert_bit_exact(got, oracle.gemm(A, B), f"report size {n}")
+
+
 # ---------------------------------------------------------------------------
 # Every configuration on ragged shapes: several tiles plus a partial one in
 # each dimension, K not a multiple of the panel depth.
