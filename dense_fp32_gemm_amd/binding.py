@@ -21,6 +21,8 @@ GEMM_F32_ERR_NULL = 3
 GEMM_F32_ERR_LAUNCH = 4
 GEMM_F32_ERR_CONFIG = 5
 GEMM_F32_ERR_ALIGN = 6
+GEMM_F32_ERR_SCRATCH = 7
+GEMM_F32_SCRATCH_BYTES = 4 << 20
 
 _lib = None
 
@@ -58,6 +60,8 @@ def load() -> ctypes.CDLL:
         lib.gemm_f32_ws_size.restype = ctypes.c_size_t
         lib.gemm_f32_ws.argtypes = [i, i, i, p, i, p, i, p, i, p, ctypes.c_size_t, p]
         lib.gemm_f32_ws.restype = i
+        lib.gemm_f32_ws_noalloc.argtypes = gemm_args
+        lib.gemm_f32_ws_noalloc.restype = i
         lib.gemm_f32_device_peak.argtypes = [i, ip, ip, ctypes.POINTER(ctypes.c_double)]
         lib.gemm_f32_device_peak.restype = i
         lib.gemm_f32_status_string.argtypes = [i]
@@ -123,6 +127,13 @@ def gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, str
     """C := A . B, split over K through `workspace` when the shape calls for it."""
     _ints(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
     return load().gemm_f32_ws(M, N, K, A, lda, B, ldb, C, ldc, workspace, workspace_bytes, stream)
+
+
+def gemm_f32_ws_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream=0) -> int:
+    """C := A . B like gemm_f32_ws, split over K through the library's own
+    static scratch (allocates nothing; overlapping calls on one GPU race)."""
+    _ints(M=M, N=N, K=K, lda=lda, ldb=ldb, ldc=ldc)
+    return load().gemm_f32_ws_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream)
 
 
 def gemm_f32_device_peak(device: int = 0) -> dict:

@@ -1899,9 +1899,64 @@ int run_workspace(int M, int N, int K, const float *A, int lda, const float *B, 
     return hipGetLastError() == hipSuccess ? GEMM_F32_OK : GEMM_F32_ERR_LAUNCH;
 }
 
+// Split-K scratch that the library owns, for callers that cannot allocate
+// (gemm_f32_ws_noalloc): one array per device, held until the process ends.
+// A split plan runs at most one 64 x 64 tile slice per compute unit, so its
+// slabs hold at most 256 x 64 x 64 floats on a whole MI355X: 4 MiB covers
+// every split plan there (a device with more compute units can need more,
+// and such plans are refused).  In host code `scratch` names a host-side
+// stand-in, never the device array: kernels and copies get the per-device
+// address hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = GEMM_F32_SCRATCH_BYTES;
+static_assert(kScratchBytes == size_t(256) * 64 * 64 * sizeof(float), "one 64 x 64 slab per compute unit");
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (resolved on the first call on that
+// device, with it current), or nullptr if it cannot be resolved.
+void *scratch_on_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    void *ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    return ptr;
+}
+
+int run_noalloc(int M, int N, int K, const float *A, int lda, const float *B, int ldb, float *C, int ldc,
+                hipStream_t stream)
+{
+    Plan p;
+    const int rc = make_plan(-1, M, N, K, A, lda, B, ldb, C, ldc, &p);
+    if (rc != GEMM_F32_OK || p.grid == 0 || K == 0)
+        return run(-1, M, N, K, A, lda, B, ldb, C, ldc, stream);   // nothing split, nothing allocated
+    if (splitk_bytes(M, N, K) > kScratchBytes)
+        return GEMM_F32_ERR_SCRATCH;
+    void *ws = scratch_on_current_device();
+    if (ws == nullptr)
+        return GEMM_F32_ERR_LAUNCH;
+    return run_workspace(M, N, K, A, lda, B, ldb, C, ldc, ws, kScratchBytes, stream);
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_f32_ws_noalloc(int M, int N, int K, const float *A, int lda, const float *B, int ldb,
+                        float *C, int ldc, hipStream_t stream)
+{
+    return run_noalloc(M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
 
 size_t gemm_f32_ws_size(int M, int N, int K)
 {
@@ -2007,6 +2062,7 @@ const char *gemm_f32_status_string(int status)
     case GEMM_F32_ERR_LAUNCH: return "kernel launch failed";
     case GEMM_F32_ERR_CONFIG: return "unknown kernel configuration";
     case GEMM_F32_ERR_ALIGN: return "a pointer is not 4-byte aligned";
+    case GEMM_F32_ERR_SCRATCH: return "the split plan needs more than the library's static scratch holds";
     default: return "unknown status";
     }
 }

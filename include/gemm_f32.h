@@ -77,6 +77,8 @@ extern "C" {
 #define GEMM_F32_ERR_LAUNCH  4  /* the HIP runtime refused the kernel launch    */
 #define GEMM_F32_ERR_CONFIG  5  /* unknown configuration index                 */
 #define GEMM_F32_ERR_ALIGN   6  /* a pointer is not 4-byte aligned              */
+#define GEMM_F32_ERR_SCRATCH 7  /* gemm_f32_ws_noalloc: the split plan needs
+                                   more than GEMM_F32_SCRATCH_BYTES            */
 
 /*
  * C := A . B on `stream`, with the kernel configuration chosen for the shape
@@ -130,6 +132,35 @@ GEMM_F32_API int gemm_f32_ws(int M, int N, int K,
                              float *C, int ldc,
                              void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product and split-K plan as gemm_f32_ws(), with the workspace taken from a
+ * scratch array the library holds in device memory, GEMM_F32_SCRATCH_BYTES
+ * per GPU (a static __device__ array, resident on each GPU the library runs
+ * on until the process ends).  The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine.  Its address on the current device
+ * is resolved once, on the first call on that device.
+ *
+ * 4 MiB holds every split plan on a whole MI355X (at most one 64 x 64 slab
+ * per compute unit); a plan that needs more (a device with more compute
+ * units) returns GEMM_F32_ERR_SCRATCH and enqueues nothing.  Shapes that are
+ * not split run exactly what gemm_f32() runs.  Validation and the other
+ * return codes are gemm_f32()'s.
+ *
+ * All calls on one GPU share its scratch array, which keeps the last call's
+ * partial products (every slab element is written before it is read, so
+ * nothing needs clearing): calls that overlap in time on one GPU (several
+ * streams, or several host threads) race and give wrong results.  Order
+ * them on one stream, or use gemm_f32_ws() with a workspace per stream.
+ */
+#define GEMM_F32_SCRATCH_BYTES ((size_t)4 << 20)
+GEMM_F32_API int gemm_f32_ws_noalloc(int M, int N, int K,
+                                     const float *A, int lda,
+                                     const float *B, int ldb,
+                                     float *C, int ldc,
+                                     hipStream_t stream);
 
 /* Number of kernel configurations, and the name of one ("" if unknown). */
 GEMM_F32_API int gemm_f32_num_configs(void);

@@ -354,3 +354,27 @@ def test_describe_names_plans_that_add_into_c():
     wb_sk = gb.config_names().index("dma_64x64x32_sk")
     rc, text = gb.gemm_f32_describe(wb_sk, 2049, 4097, 40, FAKE, 40, FAKE, 4097, FAKE, 4097)
     assert text.endswith(" c_store=write_back c_accumulate=atomic_add"), text
+
+
+def test_noalloc_entry_point_validates_like_gemm_f32():
+    f = gb.gemm_f32_ws_noalloc
+    assert f(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_DIM
+    assert f(5, 9, 8, FAKE, 7, FAKE, 9, FAKE, 9, 0) == gb.GEMM_F32_ERR_LD
+    assert f(5, 9, 8, 0, 8, FAKE, 9, FAKE, 9, 0) == gb.GEMM_F32_ERR_NULL
+    assert f(5, 9, 8, FAKE + 2, 8, FAKE, 9, FAKE, 9, 0) == gb.GEMM_F32_ERR_ALIGN
+    assert f(0, 9, 8, 0, 8, 0, 9, 0, 9, 0) == gb.GEMM_F32_OK
+    assert gb.gemm_f32_status_string(gb.GEMM_F32_ERR_SCRATCH) != "unknown status"
+    text = open(HEADER).read()
+    assert re.search(r"#define GEMM_F32_SCRATCH_BYTES \(\(size_t\)4 << 20\)", text)
+    assert gb.GEMM_F32_SCRATCH_BYTES == 4 << 20
+
+
+def test_every_split_plan_fits_the_static_scratch():
+    """A split plan runs at most one 64 x 64 slab per compute unit (256 on a
+    whole MI355X), so the 4 MiB scratch holds every one of them."""
+    worst = 0
+    for M in (16, 64, 65, 100, 128, 200, 256, 300, 640, 700, 1000, 1024):
+        for N in (16, 64, 65, 100, 128, 200, 256, 300, 640, 700, 1000, 1024):
+            for K in (256, 1024, 4096, 20000, 100000):
+                worst = max(worst, gb.gemm_f32_ws_size(M, N, K))
+    assert 0 < worst <= gb.GEMM_F32_SCRATCH_BYTES, worst
