@@ -2,7 +2,7 @@
 """Benchmark: FP32 GEMM TFLOPS and fraction of the MI355X FP32 matrix peak.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 10] [--shape M N K]
-                    [--config C] [--table] [--no-cpu-baseline]
+                    [--config C] [--table] [--single] [--no-cpu-baseline]
 
 A step is one gemm_f32 call (the whole hot path) on synthetic uniform[-1,1)
 operands already resident in HBM.  The default workload is M = N = K = 8192.
@@ -207,6 +207,8 @@ def main():
     ap.add_argument("--config", type=int, default=-1)
     ap.add_argument("--table", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--single", action="store_true",
+                    help="time only the --shape workload (skip the 2048^3 leg), e.g. to profile one shape")
     ap.add_argument("--calibrate-mib", type=int, default=0,
                     help="also run an elementwise copy (torch.neg) of this many MiB, "
                          "the known-size kernel that scales HBM byte counters")
@@ -244,7 +246,7 @@ def main():
     # The metric is quoted at 2048^3 as well: time it on every run (about a
     # second) and report it beside the headline workload.
     second = None
-    if (M, N, K) != SECOND_SHAPE:
+    if (M, N, K) != SECOND_SHAPE and not args.single:
         second = time_gemm(torch, gb, *SECOND_SHAPE, args.steps, args.warmup, args.config, min_warm_s=0.2)
         log(json.dumps(second))
     extra = {}
