@@ -427,7 +427,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     static_assert(!STRIP || (std::is_same<T, StripTile>::value && !SK && !SPLIT),
                   "remainder strips: data-parallel launches of the strip tile");
     static_assert(BK == 16 || BK == 32 || BK == 64, "the A layout permutes the 16-byte chunks of 16-, 32- or 64-deep rows");
-    static_assert(BN % 64 == 0, "the B layout swaps 32-column halves");
+    // B panels 64 or more columns wide swap 32-column halves between rows
+    // with bit 2 of k set and clear; 32-wide ones swap neighbouring rows.
+    static_assert(BN % 64 == 0 || BN == 32, "B-panel layouts exist for 32 and multiples of 64 columns");
+    constexpr bool kNarrowB = BN == 32;
     constexpr int kA = BM * BK;                       // floats per A panel
     constexpr int kB = BK * BN;                       // floats per B panel
     constexpr int kStage = kA + kB;
@@ -453,7 +456,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     // The 128-bit C epilogue stages kWaveM x BN floats in the panel buffers.
     // It pays where writing C weighs most, the 4-wave tiles chosen for short
     // K; on the 16-wave tiles of long-K problems it measured 0.4-0.8 % slower.
-    constexpr bool kBandEpilogue = KS == 1 && NW == 4 && T::kWaveM * BN <= S * kStage;
+    constexpr bool kBandEpilogue = KS == 1 && NW == 4 && BN >= 64 && T::kWaveM * BN <= S * kStage;
     static_assert(S >= 2 && (S - 2) * kLoads <= 63, "vmcnt range");
     static_assert(S == 2 || (kEvenA && kEvenB), "partial vmcnt waits need equal per-wave load counts");
     static_assert(KS * S * kStage * 4 <= 160 * 1024, "LDS budget");
@@ -493,8 +496,12 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
         const int f = (lw * kLoadsB + j) * kSpanB + lane * kVecB;
-        const int k = f / BN;
-        const int c = (f % BN) ^ (((k >> 2) & 1) * 32);
+        // Wide panels: slot (k, col) holds B(k, col ^ 32) in rows with bit 2
+        // of k set.  32-wide panels: slot row p holds B row p ^ bit 2 of p
+        // (rows 4..7 of every 8 swapped in pairs), so the two lane halves of
+        // a fragment read (rows k and k + 4) fall on different banks.
+        const int k = kNarrowB ? (f / BN) ^ ((f / BN >> 2) & 1) : f / BN;
+        const int c = kNarrowB ? f % BN : (f % BN) ^ (((k >> 2) & 1) * 32);
         b_k[j] = k;
         b_c[j] = c;
         b_off[j] = (uint32_t)(k * g.ldb + c) * 4u;
@@ -508,10 +515,18 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     // Column of fragment j after the half swap of rows with bit 2 of k set
     // (k = 8q + 4*lh + s, so that bit is lh); the fragment base is a multiple
     // of 32, so the swap only flips its bit 5.
+    // For 32-wide panels, row 8q + 4*lh + s sits in slot row 8q + 4*lh +
+    // (s ^ lh): b_frag then holds the lane's slot in row 8q + 4*lh and
+    // b_s[s] the offset of its s-th row.
     int b_frag[FN];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-        b_frag[j] = kA + (4 * lh) * BN + (((wave_n * T::kWaveN + 32 * j) ^ (32 * lh)) + li);
+        b_frag[j] = kNarrowB ? kA + (4 * lh) * BN + li
+                             : kA + (4 * lh) * BN + (((wave_n * T::kWaveN + 32 * j) ^ (32 * lh)) + li);
+    int b_s[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        b_s[s] = (kNarrowB ? (s ^ lh) : s) * BN;
 
     float (*stage)[kStage] = lds[group];   // this group's ring of S buffers
 
@@ -612,7 +627,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
-                    f.b[s][j] = pb[b_frag[j] + (8 * q + s) * BN];
+                    f.b[s][j] = pb[b_frag[j] + 8 * q * BN + b_s[s]];
         };
         // The instructions s0 .. s1-1 of a k-group (all 32 x 32 blocks).
         auto mma_part = [&](const Frag &f, int s0, int s1) {
@@ -833,17 +848,21 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             // after it (up to S-2 of them, kLoads each) are outstanding; the
             // LDS reads of round it-1 are complete as well.  Then the barrier
             // makes every wave's panel visible and frees buffer (it-1) % S.
+            // A one-wave group owns its buffers, loads its own panels and
+            // reads and writes LDS in program order: it needs no barrier.
             if (S > 2 && exists(it + S - 2))
                 asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"((S - 2) * kLoads) : "memory");
             else
                 asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
+            if constexpr (NW > 1)
+                __builtin_amdgcn_s_barrier();
             if (more)
                 fire((it + S - 1) % S, next);
             if (a_tail && it == tail_round) {
                 if (group == tail_group)
                     clear_a_tail(it % S);
-                __syncthreads();
+                if constexpr (NW > 1)
+                    __syncthreads();
             }
             if (exists(it)) {
 #pragma unroll
@@ -1261,6 +1280,15 @@ using Tile64x64K16S8P = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
 // three workgroups per CU)
 using Tile128x128K16P = MfmaTile<128, 128, 16, 2, 2, 1, 2, 8, 0, 1>;
 
+// 32-row or 32-column tiles of K-split one-wave groups, for problems with
+// few output tiles: each wave owns the whole tile for every KS-th K-panel
+// and streams those panels through its own ring of LDS buffers, with no
+// barrier until the groups' partial sums are folded.
+using Tile32x32K32S8 = MfmaTile<32, 32, 32, 1, 1, 8, 2>;   // 8 groups, 128 KiB of LDS
+using Tile32x32K32S4 = MfmaTile<32, 32, 32, 1, 1, 4, 2>;   // 4 groups, 64 KiB
+using Tile32x64K16S8 = MfmaTile<32, 64, 16, 1, 1, 8, 2>;   // 8 groups of 32 x 64, 96 KiB
+using Tile64x32K16S8 = MfmaTile<64, 32, 16, 1, 1, 8, 2>;
+
 // Every configuration is one the shape rule (select_config) picks for some
 // shapes, or the register-staged fallback for rows too long for 32-bit
 // panel offsets; each also runs under gemm_f32_with_config for tests and
@@ -1285,6 +1313,10 @@ enum ConfigId {
     kCfgDma64x64K16S8P,
     kCfgDma64x64K32S4SK,
     kCfgDma128x128K16P,
+    kCfgDma32x32K32S8,
+    kCfgDma32x32K32S4,
+    kCfgDma32x64K16S8,
+    kCfgDma64x32K16S8,
     kNumConfigs
 };
 
@@ -1428,6 +1460,10 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile64x64K16S8P, true>("dma_64x64x16_ksplit8_pipe"),
     config_streamk<Tile64x64K32S4>("dma_64x64x32_ksplit4_sk"),
     config_dma<Tile128x128K16P, true>("dma_128x128x16_pipe"),
+    config_dma<Tile32x32K32S8>("dma_32x32x32_ksplit8"),
+    config_dma<Tile32x32K32S4>("dma_32x32x32_ksplit4"),
+    config_dma<Tile32x64K16S8>("dma_32x64x16_ksplit8"),
+    config_dma<Tile64x32K16S8>("dma_64x32x16_ksplit8"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1540,6 +1576,18 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
             return kCfgStaged128x128;
         return kCfgStaged64x64;
     }
+    // Few output tiles: while 32 x 32 tiles fit in one round, one workgroup
+    // per 32 x 32 tile of 8 K-split one-wave groups keeps every CU busy
+    // (512^3: 9.4 us against 15.9 for 64 one-round 64 x 64 tiles; 256 x 256
+    // x 8192: 45 against 126; 500^3: 9.8 against 16.3); with K <= 256, 4
+    // groups (300 x 400 x 100: 6.7 against 7.2 for 8).  While 32 x 64 (64 x
+    // 32) tiles fit in one round, 8 groups of those (640 x 640 x 2048: 25.9
+    // us against 39.3; 1024 x 512 x 1024: 17.2 against 24.7).
+    const int64_t t32x32 = ceil_div(M, 32) * ceil_div(N, 32);
+    if (t32x32 <= CU)
+        return K > 256 ? kCfgDma32x32K32S8 : kCfgDma32x32K32S4;
+    if (N >= M ? tiles(kCfgDma32x64K16S8) <= CU : tiles(kCfgDma64x32K16S8) <= CU)
+        return N >= M ? kCfgDma32x64K16S8 : kCfgDma64x32K16S8;
     // The busiest CU has ceil(tiles / CUs) tiles.  The last round of tiles
     // leaves more than a fifth of the CU-rounds idle when this is true:
     auto unbalanced = [&](int c) {

@@ -188,9 +188,16 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # pipelined one-wave groups from K = 2048 on
     ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 16384, 4096), "dma_64x64x16_ksplit8_pipe "),
     ((1024, 1024, 8192), "dma_64x64x16_ksplit8_pipe "), ((100, 5000, 3000), "dma_64x64x16_ksplit8_pipe "),
-    ((1000, 1000, 1000), "dma_64x64x32_ksplit4 "), ((512, 512, 1024), "dma_64x64x32_ksplit4 "),
+    ((1000, 1000, 1000), "dma_64x64x32_ksplit4 "), ((768, 768, 1024), "dma_64x64x32_ksplit4 "),
     # K <= 512: no K split
-    ((512, 512, 512), "dma_64x64x64 "), ((1000, 1000, 300), "dma_64x64x64 "),
+    ((1000, 1000, 300), "dma_64x64x64 "),
+    # few output tiles: 32 x 32 tiles of one-wave K-split groups while they
+    # fit one round (4 groups for K <= 256), then 32 x 64 or 64 x 32 ones
+    ((512, 512, 512), "dma_32x32x32_ksplit8 "), ((512, 512, 1024), "dma_32x32x32_ksplit8 "),
+    ((256, 256, 8192), "dma_32x32x32_ksplit8 "), ((17, 33, 65), "dma_32x32x32_ksplit4 "),
+    ((300, 400, 100), "dma_32x32x32_ksplit4 "), ((64, 2048, 2048), "dma_32x32x32_ksplit8 "),
+    ((640, 640, 2048), "dma_32x64x16_ksplit8 "), ((512, 1024, 1024), "dma_32x64x16_ksplit8 "),
+    ((1024, 512, 1024), "dma_64x32x16_ksplit8 "), ((700, 600, 1000), "dma_64x32x16_ksplit8 "),
     # 272 tiles, 16 of them for a last row of 1-4 rows (rows x K <= 4096): one
     # round of K-split tiles and a strip of FMAs
     ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((1028, 1000, 1000), "dma_64x64x32_ksplit4 "),
@@ -378,3 +385,17 @@ def test_every_split_plan_fits_the_static_scratch():
             for K in (256, 1024, 4096, 20000, 100000):
                 worst = max(worst, gb.gemm_f32_ws_size(M, N, K))
     assert 0 < worst <= gb.GEMM_F32_SCRATCH_BYTES, worst
+
+
+def test_gpu_tests_plan_what_they_name():
+    """The GPU tests that name the plan a shape gets (graph capture per kernel
+    family, remainder strips) hold on the host too, so a change of the shape
+    rule shows up here before a GPU run."""
+    import ast
+    src = open(os.path.join(ROOT, "tests", "test_parity.py")).read()
+    for var, check in (("GRAPH_PLANS", lambda d, n: d.startswith(n)),
+                       ("STRIP", lambda d, n: d.endswith(" " + n))):
+        m = re.search(var + r" = (\[.*?\])\n", src, re.S)
+        for (M, N, K), name in ast.literal_eval(m.group(1)):
+            rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
+            assert rc == gb.GEMM_F32_OK and check(text, name), (var, (M, N, K), text)

@@ -26,11 +26,13 @@ def a_store(BM, BK=16):
 
 def b_store(BN, BK=16):
     """LDS slot (k, column) -> global (k, column) for one B panel."""
+    if BN == 32:      # 32-wide panels: slot row p holds B row p ^ (bit 2 of p)
+        return {(p, c): (p ^ ((p >> 2) & 1), c) for p in range(BK) for c in range(BN)}
     return {(k, c): (k, c ^ (((k >> 2) & 1) * 32)) for k in range(BK) for c in range(BN)}
 
 
 @pytest.mark.parametrize("BK", [16, 32, 64])
-@pytest.mark.parametrize("BM,WM", [(256, 2), (256, 4), (128, 2), (128, 4), (64, 2)])
+@pytest.mark.parametrize("BM,WM", [(256, 2), (256, 4), (128, 2), (128, 4), (64, 2), (32, 1)])
 def test_a_fragments_read_the_paired_k(BM, WM, BK):
     store = a_store(BM, BK)
     for wm in range(WM):
@@ -69,3 +71,23 @@ def test_layouts_are_permutations():
     for BN in (64, 128, 256):
         for k in range(64):
             assert sorted(c ^ (((k >> 2) & 1) * 32) for c in range(BN)) == list(range(BN))
+
+
+@pytest.mark.parametrize("BK", [16, 32, 64])
+def test_narrow_b_fragments_read_the_paired_k(BK):
+    """32-wide B panels: lane half lh reads logical row 8q + 4*lh + s from
+    slot row 8q + 4*lh + (s ^ lh), column li."""
+    store = b_store(32, BK)
+    for lane in range(64):
+        li, lh = lane % 32, lane // 32
+        for q in range(BK // 8):
+            for s in range(4):
+                slot_row = 8 * q + 4 * lh + (s ^ lh)
+                assert store[(slot_row, li)] == (8 * q + 4 * lh + s, li)
+    # a permutation of the panel's rows, and the two halves of every read
+    # land in different 32-float halves of a 64-float bank window
+    assert sorted(p ^ ((p >> 2) & 1) for p in range(BK)) == list(range(BK))
+    for q in range(BK // 8):
+        for s in range(4):
+            rows = [8 * q + 4 * lh + (s ^ lh) for lh in (0, 1)]
+            assert (rows[0] * 32 // 32) % 2 != (rows[1] * 32 // 32) % 2
