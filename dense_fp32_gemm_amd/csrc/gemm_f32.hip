@@ -878,97 +878,131 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         // (by the K-split reduction, or by the next tile's first loads).
         __syncthreads();
 
-        if (KS > 1) {
-            // Fold the groups' partial sums into group 0 along a fixed binary
-            // tree, through LDS laid out as C's tile: at distance d = 1, 2,
-            // 4, ... group g with g % 2d == d hands its sum to group g - d
-            // through a region of its own, so each step's additions run in
-            // parallel and their order never changes (8 one-wave groups:
-            // 16384 x 64 x 4096 67.8 us against 68.6 for folding one group
-            // after another).  The panel buffers are free: the loop ended
-            // with a barrier.
-            static_assert((KS & (KS - 1)) == 0, "tree fold over a power-of-two number of groups");
-            static_assert(KS / 2 * BM * BN <= KS * S * kStage, "fold regions fit in the panel buffers");
-            for (int d = 1; d < KS; d *= 2) {
-                float *red = &lds[0][0][0] + (group / (2 * d)) * (BM * BN);
-                if (group % (2 * d) == d) {
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int row = wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                                red[row * BN + wave_n * T::kWaveN + j * 32 + li] = acc[i][j][r];
-                            }
-                }
-                __syncthreads();
-                if (group % (2 * d) == 0) {
-#pragma unroll
-                    for (int i = 0; i < FM; ++i)
-#pragma unroll
-                        for (int j = 0; j < FN; ++j)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int row = wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                                acc[i][j][r] += red[row * BN + wave_n * T::kWaveN + j * 32 + li];
-                            }
-                }
-                __syncthreads();
-            }
-        }
-
         const bool shared = SK && (p_begin != 0 || p_end != ktiles);
-        if (kBandEpilogue && !shared && c_vec && m0 + BM <= g.M && n0 + BN <= g.N) {
-            // Whole tile, 16-byte aligned rows of C: stage one band of
-            // kWaveM rows at a time through the (now idle) panel buffers and
-            // write C with 128-bit stores of whole rows instead of one
-            // 32-bit store per accumulator element (+3.5 to +7 % on
-            // 8192 x 8192 x 128, whose time is dominated by writing C).  The
-            // band is [kWaveM][BN]; rows with bit 2 set have their columns
-            // swapped in 32-float halves, so the two lane halves of an
-            // accumulator write (rows 4 apart) fall on different banks.
-            float *band = &lds[0][0][0];
-            for (int p = 0; p < T::WAVES_M; ++p) {
-                if (wave_m == p) {
+        if constexpr (KS > 1) {
+            // Fold the groups' partial sums and write C: every group stores
+            // its partial tile into a region of its own (the panel buffers
+            // are free: the loop ended with a barrier), then, after one
+            // barrier, each thread adds a 4-column chunk of the groups'
+            // partials in group order 0, 1, ..., KS-1 -- a fixed order, so
+            // the result does not depend on scheduling -- and writes it to
+            // C as one 128-bit store (element by element in edge tiles, for
+            // unaligned rows, and as atomic adds in stream-K's shared
+            // tiles).  In a region, rows with bit 2 set have their columns
+            // swapped in 32-float halves (32-wide tiles: their rows swapped
+            // in pairs), so the two lane halves of an accumulator write
+            // (rows 4 apart) fall on different banks.
+            static_assert(KS * BM * BN <= KS * S * kStage, "every group's partial tile fits in the panel buffers");
+            float *part = &lds[0][0][0];
+            auto slot = [](int row, int col) {
+                return kNarrowB ? (row ^ ((row >> 2) & 1)) * BN + col : row * BN + (col ^ ((row & 4) ? 32 : 0));
+            };
+            float *mine = part + group * (BM * BN);
 #pragma unroll
-                    for (int i = 0; i < FM; ++i)
+            for (int i = 0; i < FM; ++i)
 #pragma unroll
-                        for (int j = 0; j < FN; ++j)
-#pragma unroll
-                            for (int r = 0; r < 16; ++r) {
-                                const int lr = i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                                const int lc = (wave_n * T::kWaveN + j * 32 + li) ^ ((lr & 4) ? 32 : 0);
-                                band[lr * BN + lc] = acc[i][j][r];
-                            }
-                }
-                __syncthreads();
-                constexpr int kRowChunks = BN / 4;
-                for (int e = tid; e < T::kWaveM * kRowChunks; e += T::kThreads) {
-                    const int lr = e / kRowChunks, c4 = e % kRowChunks;
-                    const f32x4 v = *reinterpret_cast<const f32x4 *>(&band[lr * BN + ((4 * c4) ^ ((lr & 4) ? 32 : 0))]);
-                    float *dst = &cbase[(int64_t)(m0 + p * T::kWaveM + lr) * g.ldc + n0 + 4 * c4];
-                    __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
-                }
-                __syncthreads();
-            }
-            return;
-        }
-        if (group == 0) {
-#pragma unroll
-            for (int i = 0; i < FM; ++i) {
-#pragma unroll
-                for (int j = 0; j < FN; ++j) {
-                    const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
+                for (int j = 0; j < FN; ++j)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
-                        if (row < g.M && col < g.N) {
-                            float *c = &cbase[(int64_t)row * g.ldc + col];
-                            if (shared)
-                                unsafeAtomicAdd(c, acc[i][j][r]);
-                            else
-                                store_c<WB>(c, acc[i][j][r]);
+                        const int row = wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                        mine[slot(row, wave_n * T::kWaveN + j * 32 + li)] = acc[i][j][r];
+                    }
+            __syncthreads();
+            auto sum = [&](int at) {
+                float v = part[at];
+#pragma unroll
+                for (int q = 1; q < KS; ++q)
+                    v += part[q * (BM * BN) + at];
+                return v;
+            };
+            if (!shared && c_vec && m0 + BM <= g.M && n0 + BN <= g.N) {
+                constexpr int kRowChunks = BN / 4;
+                for (int e = tid; e < BM * kRowChunks; e += T::kThreads) {
+                    const int lr = e / kRowChunks, lc = 4 * (e % kRowChunks);
+                    const int at = slot(lr, lc);
+                    f32x4 v = *reinterpret_cast<const f32x4 *>(&part[at]);
+#pragma unroll
+                    for (int q = 1; q < KS; ++q)
+                        v += *reinterpret_cast<const f32x4 *>(&part[q * (BM * BN) + at]);
+                    float *c = &cbase[(int64_t)(m0 + lr) * g.ldc + n0 + lc];
+                    if constexpr (WB)
+                        *reinterpret_cast<f32x4 *>(c) = v;
+                    else
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(c));
+                }
+            } else {
+                // Edge tiles, unaligned rows and shared tiles: one element
+                // per thread, consecutive threads on consecutive columns, so
+                // each store (or atomic add) instruction covers whole runs
+                // of a row.
+                for (int e = tid; e < BM * BN; e += T::kThreads) {
+                    const int lr = e / BN, lc = e % BN;
+                    const int row = m0 + lr, col = n0 + lc;
+                    if (row < g.M && col < g.N) {
+                        const float v = sum(slot(lr, lc));
+                        float *c = &cbase[(int64_t)row * g.ldc + col];
+                        if (shared)
+                            unsafeAtomicAdd(c, v);
+                        else
+                            store_c<WB>(c, v);
+                    }
+                }
+            }
+            // Every thread is done with the regions before the panel buffers
+            // are reused (a strip's sums, or the next tile's loads).
+            __syncthreads();
+        } else {
+            if (kBandEpilogue && !shared && c_vec && m0 + BM <= g.M && n0 + BN <= g.N) {
+                // Whole tile, 16-byte aligned rows of C: stage one band of
+                // kWaveM rows at a time through the (now idle) panel buffers and
+                // write C with 128-bit stores of whole rows instead of one
+                // 32-bit store per accumulator element (+3.5 to +7 % on
+                // 8192 x 8192 x 128, whose time is dominated by writing C).  The
+                // band is [kWaveM][BN]; rows with bit 2 set have their columns
+                // swapped in 32-float halves, so the two lane halves of an
+                // accumulator write (rows 4 apart) fall on different banks.
+                float *band = &lds[0][0][0];
+                for (int p = 0; p < T::WAVES_M; ++p) {
+                    if (wave_m == p) {
+#pragma unroll
+                        for (int i = 0; i < FM; ++i)
+#pragma unroll
+                            for (int j = 0; j < FN; ++j)
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    const int lr = i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                                    const int lc = (wave_n * T::kWaveN + j * 32 + li) ^ ((lr & 4) ? 32 : 0);
+                                    band[lr * BN + lc] = acc[i][j][r];
+                                }
+                    }
+                    __syncthreads();
+                    constexpr int kRowChunks = BN / 4;
+                    for (int e = tid; e < T::kWaveM * kRowChunks; e += T::kThreads) {
+                        const int lr = e / kRowChunks, c4 = e % kRowChunks;
+                        const f32x4 v = *reinterpret_cast<const f32x4 *>(&band[lr * BN + ((4 * c4) ^ ((lr & 4) ? 32 : 0))]);
+                        float *dst = &cbase[(int64_t)(m0 + p * T::kWaveM + lr) * g.ldc + n0 + 4 * c4];
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
+                    }
+                    __syncthreads();
+                }
+                return;
+            }
+            if (group == 0) {
+#pragma unroll
+                for (int i = 0; i < FM; ++i) {
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int col = n0 + wave_n * T::kWaveN + j * 32 + li;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int row = m0 + wave_m * T::kWaveM + i * 32 + 8 * (r / 4) + 4 * lh + (r % 4);
+                            if (row < g.M && col < g.N) {
+                                float *c = &cbase[(int64_t)row * g.ldc + col];
+                                if (shared)
+                                    unsafeAtomicAdd(c, acc[i][j][r]);
+                                else
+                                    store_c<WB>(c, acc[i][j][r]);
+                            }
                         }
                     }
                 }
