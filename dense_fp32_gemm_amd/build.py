@@ -1,6 +1,6 @@
 """Builds libgemm_f32.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m dense_fp32_gemm_amd.build [--verbose]
+    python -m dense_fp32_gemm_amd.build [--verbose] [--poison-lds]
 
 hipcc compiles for gfx950 only.  Packed-FP32 instruction selection is turned
 off for device code (-Xclang -target-feature -Xclang -packed-fp32-ops); the
@@ -28,10 +28,23 @@ HIPFLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra: list[str] | None = None) -> str:
+# Debug build: -DGEMM_F32_POISON_LDS makes the kernels set every LDS slot to
+# NaN before it is refilled or first written (see kPoisonLds in the source),
+# so a stale LDS read shows up as NaN in C.  gemm_f32_describe() then ends
+# with " lds=poisoned".
+POISON_LDS = "-DGEMM_F32_POISON_LDS"
+
+
+def command(out: str, extra: list[str] | None = None, poison_lds: bool = False) -> list[str]:
+    """The hipcc command line that builds the library into `out`."""
+    flags = [*HIPFLAGS, *([POISON_LDS] if poison_lds else []), *(extra or [])]
+    return ["hipcc", *flags, "-I", INCLUDE, *SOURCES, "-o", out]
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, poison_lds: bool = False) -> str:
     """Compile the library; returns its path.  Always recompiles."""
     tmp = LIBRARY + ".tmp%d" % os.getpid()
-    cmd = ["hipcc", *HIPFLAGS, *(extra or []), "-I", INCLUDE, *SOURCES, "-o", tmp]
+    cmd = command(tmp, extra, poison_lds)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,5 +59,5 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose="--verbose" in sys.argv)
+    build(verbose="--verbose" in sys.argv, poison_lds="--poison-lds" in sys.argv)
     print(LIBRARY)

@@ -395,6 +395,32 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma(GemmArgs g)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset that reads as 0
 constexpr int kRawBufferFlags = 0x00020000;      // dword 3 of a raw buffer resource
 
+// Debug build (-DGEMM_F32_POISON_LDS): every LDS slot a panel load is about
+// to fill is first set to NaN by the wave that issues the load, and every
+// fold, band and strip region is set to NaN before it is written.  A read of
+// a slot before its data has landed, or of a region slot nobody wrote, then
+// carries NaN into C, which every parity check catches; with the normal
+// build such a read would pick up stale but finite values.
+#ifdef GEMM_F32_POISON_LDS
+constexpr bool kPoisonLds = true;
+#else
+constexpr bool kPoisonLds = false;
+#endif
+
+__device__ inline void poison16(float *p)
+{
+    const float nan = __builtin_nanf("");
+    *reinterpret_cast<f32x4 *>(p) = f32x4{nan, nan, nan, nan};
+}
+
+// NaN over `floats` floats of LDS from `base` (16-byte aligned, a multiple
+// of 4 floats), by `threads` threads of which this is thread `t`.
+__device__ inline void poison_region(float *base, int floats, int t, int threads)
+{
+    for (int e = 4 * t; e < floats; e += 4 * threads)
+        poison16(base + e);
+}
+
 // Chunk permutation of A-panel row r (BK/4 chunks of 16 bytes per row).
 // Chosen by measurement (SQ_LDS_BANK_CONFLICT on 128-bit fragment reads of
 // 32 consecutive rows): for 64-byte rows, rows four apart share banks and
@@ -584,6 +610,17 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         auto fire = [&](int buf, const Panel &p) {
             if (NL < NW && !loader)
                 return;
+            if constexpr (kPoisonLds) {
+#pragma unroll
+                for (int j = 0; j < kLoadsA; ++j)
+                    if (kEvenA || lw * kLoadsA + j < kInstA)
+                        poison16(&stage[buf][(lw * kLoadsA + j) * kSpanA + lane * kVecA]);
+#pragma unroll
+                for (int j = 0; j < kLoadsB; ++j)
+                    if (kEvenB || lw * kLoadsB + j < kInstB)
+                        poison16(&stage[buf][kA + (lw * kLoadsB + j) * kSpanB + lane * kVecB]);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
             const __amdgpu_buffer_rsrc_t ra =
                 __builtin_amdgcn_make_buffer_rsrc((void *)p.a, 0, p.a_range, kRawBufferFlags);
             const __amdgpu_buffer_rsrc_t rb =
@@ -746,6 +783,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                                                               kRawBufferFlags)};
             };
             // Load x of a wave's panel share (A's loads first, then B's).
+            // Debug build: NaN into every slot this wave's loads of one
+            // round fill, before they are issued.
+            auto poison_loads = [&](int buf) {
+                if constexpr (kPoisonLds) {
+#pragma unroll
+                    for (int x = 0; x < kLoadsA; ++x)
+                        poison16(&stage[buf][(lw * kLoadsA + x) * kSpanA + lane * kVecA]);
+#pragma unroll
+                    for (int x = 0; x < kLoadsB; ++x)
+                        poison16(&stage[buf][kA + (lw * kLoadsB + x) * kSpanB + lane * kVecB]);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                }
+            };
             auto load_one = [&](int buf, const Rsrc &r, int x) {
                 if (x < kLoadsA)
                     buffer_to_lds(r.a, &stage[buf][(lw * kLoadsA + x) * kSpanA], oa_t[x]);
@@ -775,6 +825,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             if (my_rounds > 0) {
             {
                 const Rsrc r0 = rsrc(panel_k(0), true);
+                poison_loads(0);
 #pragma unroll
                 for (int x = 0; x < kLoads; ++x)
                     load_one(0, r0, x);
@@ -791,6 +842,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             for (int it = 0; it < my_rounds; ++it) {
                 const int buf = it & 1;
                 const Rsrc nx = rsrc(panel_k(it + 1), it + 1 < my_rounds);
+                poison_loads(buf ^ 1);
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int q = 0; q + 1 < Q; ++q) {
@@ -898,6 +950,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 return kNarrowB ? (row ^ ((row >> 2) & 1)) * BN + col : row * BN + (col ^ ((row & 4) ? 32 : 0));
             };
             float *mine = part + group * (BM * BN);
+            if constexpr (kPoisonLds) {
+                poison_region(part, KS * BM * BN, tid, T::kThreads);
+                __syncthreads();
+            }
 #pragma unroll
             for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -963,6 +1019,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 // accumulator write (rows 4 apart) fall on different banks.
                 float *band = &lds[0][0][0];
                 for (int p = 0; p < T::WAVES_M; ++p) {
+                    if constexpr (kPoisonLds) {
+                        poison_region(band, T::kWaveM * BN, tid, T::kThreads);
+                        __syncthreads();
+                    }
                     if (wave_m == p) {
 #pragma unroll
                         for (int i = 0; i < FM; ++i)
@@ -1029,6 +1089,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             float *red = &lds[0][0][0];
             float *sa = red + kRed;                  // strip_rows x K floats of A
             __syncthreads();
+            if constexpr (kPoisonLds) {
+                poison_region(red, (kRed + g.strip_rows * g.K + 3) / 4 * 4, tid, T::kThreads);
+                __syncthreads();
+            }
             for (int e = tid; e < g.strip_rows * g.K; e += T::kThreads)
                 sa[e] = g.A[(int64_t)(r0 + e / g.K) * g.lda + e % g.K];
             __syncthreads();
@@ -1095,6 +1159,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             float *red = &lds[0][0][0];
             float *sb = red + kRed;                  // strip_cols x K floats of B, as [c][k]
             __syncthreads();
+            if constexpr (kPoisonLds) {
+                poison_region(red, (kRed + g.strip_cols * g.K + 3) / 4 * 4, tid, T::kThreads);
+                __syncthreads();
+            }
             for (int e = tid; e < g.strip_cols * g.K; e += T::kThreads)
                 sb[e] = g.B[(int64_t)(e % g.K) * g.ldb + c0 + e / g.K];
             __syncthreads();
@@ -2127,9 +2195,12 @@ int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
             snprintf(buf + n, (size_t)(buflen - n), " strip_cols=%d", p.strip_cols);
         else if (p.wb_c && n >= 0 && n < buflen)
             snprintf(buf + n, (size_t)(buflen - n), " c_store=write_back");
-        const int used = (int)strlen(buf);
+        int used = (int)strlen(buf);
         if (p.shares_tiles && used + 1 < buflen)
             snprintf(buf + used, (size_t)(buflen - used), " c_accumulate=atomic_add");
+        used = (int)strlen(buf);
+        if (kPoisonLds && used + 1 < buflen)
+            snprintf(buf + used, (size_t)(buflen - used), " lds=poisoned");
     }
     return rc;
 }

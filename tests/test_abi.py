@@ -399,3 +399,16 @@ def test_gpu_tests_plan_what_they_name():
         for (M, N, K), name in ast.literal_eval(m.group(1)):
             rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
             assert rc == gb.GEMM_F32_OK and check(text, name), (var, (M, N, K), text)
+
+
+def test_poison_lds_flag_reaches_hipcc():
+    from dense_fp32_gemm_amd import build
+    cmd = build.command("/tmp/x.so", poison_lds=True)
+    assert cmd[0] == "hipcc" and "-DGEMM_F32_POISON_LDS" in cmd
+    assert "-DGEMM_F32_POISON_LDS" not in build.command("/tmp/x.so")
+    assert "--offload-arch=gfx950" in cmd
+    src = open(os.path.join(ROOT, "dense_fp32_gemm_amd", "csrc", "gemm_f32.hip")).read()
+    assert "#ifdef GEMM_F32_POISON_LDS" in src
+    # the normal build is not the poisoned one
+    rc, text = gb.gemm_f32_describe(-1, 512, 512, 512, FAKE, 512, FAKE, 512, FAKE, 512)
+    assert "poison" not in text, text
