@@ -1382,6 +1382,10 @@ using Tile64x64K16S8P = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
 // three workgroups per CU)
 using Tile128x128K16P = MfmaTile<128, 128, 16, 2, 2, 1, 2, 8, 0, 1>;
 
+// Software-pipelined 4 waves of 64 x 64 on 32-deep panels (64 KiB of LDS,
+// two workgroups per CU)
+using Tile128x128K32P = MfmaTile<128, 128, 32, 2, 2, 1, 2, 8, 0, 1>;
+
 // 32-row or 32-column tiles of K-split one-wave groups, for problems with
 // few output tiles: each wave owns the whole tile for every KS-th K-panel
 // and streams those panels through its own ring of LDS buffers, with no
@@ -1419,6 +1423,7 @@ enum ConfigId {
     kCfgDma32x32K32S4,
     kCfgDma32x64K16S8,
     kCfgDma64x32K16S8,
+    kCfgDma128x128K32P,
     kNumConfigs
 };
 
@@ -1566,6 +1571,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile32x32K32S4>("dma_32x32x32_ksplit4"),
     config_dma<Tile32x64K16S8>("dma_32x64x16_ksplit8"),
     config_dma<Tile64x32K16S8>("dma_64x32x16_ksplit8"),
+    config_dma<Tile128x128K32P, true>("dma_128x128x32_pipe"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1733,17 +1739,22 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     const int64_t t128 = tiles(kCfgDma128x128K64P);
     if (!thin && t128 >= CU) {
         if (!streamk_pays(kCfgDma128x128K64P)) {
-            // Two or more rounds with K < 2048, or eight and more with any K:
-            // three resident workgroups of the 16-deep pipelined tile overlap
-            // each other's start-up and stores (6000 x 2000 x 1000: 185 us
-            // against 198; 6478 x 5640 x 3472: 1796 against 1856).
-            if (t128 >= 2 * CU && (K < 2048 || t128 >= 8 * CU))
+            // Three or more rounds: three resident workgroups of the 16-deep
+            // pipelined tile overlap each other's start-up and stores
+            // (6000 x 2000 x 1000: 185 us against 198; 6144 x 2048 x 4096: 717
+            // against 727 for 64-deep panels; 6478 x 5640 x 3472: 1796 against
+            // 1856).  Two rounds: two resident workgroups of the 32-deep one
+            // (4096 x 2048 x 2048: 243 against 248 for 64-deep panels and 250
+            // for 16-deep ones; 4096 x 2048 x 1024: 125.5 against 128.5).
+            if (t128 > 2 * CU || (t128 == 2 * CU && K < 512))
                 return kCfgDma128x128K16P;
             // One or two rounds with a short K: a 64-deep panel ring has
             // too few rounds to fill; 64 x 64 tiles balance better
             // (5221 x 1201 x 233: 37.9 us against 50.5).
             if (K < 512)
                 return kCfgDma64x64K32;
+            if (t128 > CU)
+                return kCfgDma128x128K32P;
             return deep_ok ? kCfgDma128x128K64P : kCfgDma128x128K32S2;
         }
         // Stream-K's extra launch and split-tile passes pay off over a long

@@ -121,7 +121,7 @@ def test_describe():
 WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
               "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
               "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe",
-              "dma_128x128x16_pipe"]
+              "dma_128x128x16_pipe", "dma_128x128x32_pipe"]
 
 
 def test_describe_write_back_c_stores():
@@ -181,7 +181,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
 
 @pytest.mark.parametrize("shape,name", [
     ((8192, 8192, 8192), "dma_256x256x32_pipe "), ((2048, 2048, 2048), "dma_128x128x64_pipe "),
-    ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x64_pipe "),
+    ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x32_pipe "),
     ((8192, 8192, 128), "dma_128x128x16_pipe "), ((8192, 8192, 512), "dma_128x128x16_pipe "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # at most one 64 x 64 tile per CU: K split inside the workgroup, 8
@@ -219,7 +219,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # two or more balanced rounds of 128 x 128 tiles: 16-deep pipelined
     # panels for K < 2048
     ((6000, 2000, 1000), "dma_128x128x16_pipe "), ((4096, 3072, 1024), "dma_128x128x16_pipe "),
-    ((4096, 2048, 2048), "dma_128x128x64_pipe "),
+    ((4096, 2048, 2048), "dma_128x128x32_pipe "), ((4096, 2048, 1024), "dma_128x128x32_pipe "),
+    ((6144, 2048, 4096), "dma_128x128x16_pipe "), ((2048, 2048, 1024), "dma_128x128x64_pipe "),
     # a side of at most 64 (or 129 to 192): 128-wide tiles would be mostly
     # padding, so only the 64 x 64 choices; a side of 96 or 128 keeps them
     ((64, 32768, 4096), "dma_64x64x16_ksplit8_pipe "), ((32768, 64, 4096), "dma_64x64x16_ksplit8_pipe "),

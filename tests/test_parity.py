@@ -212,7 +212,7 @@ def test_unaligned_bases(dev, config):
 WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
               "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
               "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe",
-              "dma_128x128x16_pipe"]
+              "dma_128x128x16_pipe", "dma_128x128x32_pipe"]
 
 
 @functools.lru_cache(maxsize=1)
