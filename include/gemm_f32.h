@@ -44,8 +44,10 @@
  * reported by the caller's next synchronising HIP call, not by the return
  * value.
  *
- * Degenerate shapes (the page's harness: negative sizes are an error, an
- * empty output returns at once, K = 0 leaves the sum empty):
+ * Degenerate shapes (as the harness of the UIUC ECE408 Lecture 12
+ * final-project page treats them, project_template.cu section 7: negative
+ * sizes are an error, an empty output returns at once, K = 0 leaves the sum
+ * empty):
  *   M < 0, N < 0 or K < 0  -> GEMM_F32_ERR_DIM, nothing is enqueued;
  *   M == 0 or N == 0       -> GEMM_F32_OK, nothing is enqueued, any pointer
  *                             may be NULL;
@@ -83,8 +85,12 @@ extern "C" {
 /*
  * C := A . B on `stream`, with the kernel configuration chosen for the shape
  * and operand alignment (gemm_f32_describe() names the choice).  Arguments
- * are validated in this order: sizes, leading dimensions, NULL pointers,
- * alignment; the first failure is returned and nothing is enqueued.
+ * are validated in this order: sizes (GEMM_F32_ERR_DIM), leading dimensions
+ * (GEMM_F32_ERR_LD), the configuration index where one is passed
+ * (GEMM_F32_ERR_CONFIG), NULL pointers (GEMM_F32_ERR_NULL), alignment
+ * (GEMM_F32_ERR_ALIGN); the first failure is returned and nothing is
+ * enqueued.  An empty output (M or N == 0) returns GEMM_F32_OK after the
+ * size, leading-dimension and configuration checks, whatever the pointers.
  */
 GEMM_F32_API int gemm_f32(int M, int N, int K,
              const float *A, int lda,

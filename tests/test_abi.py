@@ -77,10 +77,17 @@ def test_misaligned_pointers():
 
 
 def test_validation_order():
-    # sizes before leading dimensions before pointers before alignment
+    # sizes, leading dimensions, configuration, pointers, alignment -- the
+    # order include/gemm_f32.h states
+    bad = gb.gemm_f32_num_configs()
     assert gb.gemm_f32(-1, 4, 4, 0, 0, 0, 0, 0, 0, 0) == gb.GEMM_F32_ERR_DIM
+    assert gb.gemm_f32_with_config(bad, -1, 4, 4, 0, 0, 0, 0, 0, 0, 0) == gb.GEMM_F32_ERR_DIM
     assert gb.gemm_f32(4, 4, 4, 0, 0, 0, 4, 0, 4, 0) == gb.GEMM_F32_ERR_LD
+    assert gb.gemm_f32_with_config(bad, 4, 4, 4, 0, 0, 0, 4, 0, 4, 0) == gb.GEMM_F32_ERR_LD
+    assert gb.gemm_f32_with_config(bad, 4, 4, 4, 0, 4, 0, 4, 0, 4, 0) == gb.GEMM_F32_ERR_CONFIG
+    assert gb.gemm_f32_with_config(bad, 0, 4, 4, 0, 4, 0, 4, 0, 4, 0) == gb.GEMM_F32_ERR_CONFIG
     assert gb.gemm_f32(4, 4, 4, 0, 4, FAKE + 1, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_NULL
+    assert gb.gemm_f32(4, 4, 4, FAKE + 1, 4, FAKE, 4, FAKE, 4, 0) == gb.GEMM_F32_ERR_ALIGN
 
 
 def test_unknown_config():
