@@ -166,7 +166,7 @@ __device__ inline f32x4 load_row4(const float *p, bool row_ok, int col, int ncol
 // Tile parameters, and the register-staged matrix-core kernel
 // ---------------------------------------------------------------------------
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int KSPLIT_ = 1, int STAGES_ = 2,
-          int GROUP_ = 8, int LOADERS_ = 0, int PIPE_ = 0>
+          int GROUP_ = 8, int LOADERS_ = 0, int PIPE_ = 0, int LOADER_WAVE_ = 0>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -174,7 +174,11 @@ struct MfmaTile {
     // each accumulate every KSPLIT-th K-panel of the same output tile.
     static constexpr int kSplit = KSPLIT_;
     static constexpr int kGroupWaves = WAVES_M * WAVES_N;
-    static constexpr int kThreads = kGroupWaves * kWaveSize * kSplit;
+    // Software-pipelined tiles may add LOADER_WAVES waves that issue all
+    // panel loads while the others only read LDS and run MFMAs.
+    static constexpr int kLoaderWaves = LOADER_WAVE_;
+    static constexpr bool kLoaderWave = kLoaderWaves != 0;
+    static constexpr int kThreads = (kGroupWaves * kSplit + kLoaderWaves) * kWaveSize;
     static constexpr int kWaveM = BM / WAVES_M;      // C rows per wave
     static constexpr int kWaveN = BN / WAVES_N;      // C columns per wave
     static constexpr int kFragM = kWaveM / 32;       // 32x32 accumulators down
@@ -203,6 +207,7 @@ struct MfmaTile {
     static_assert(BM % (32 * WAVES_M) == 0 && BN % (32 * WAVES_N) == 0, "wave tile");
     static_assert(BK % 8 == 0, "BK feeds k in groups of 8");
     static_assert(kLoaders >= 1 && kLoaders <= WAVES_M * WAVES_N, "loader waves");
+    static_assert(!kLoaderWave || (PIPE_ != 0 && KSPLIT_ == 1), "loader waves serve one pipelined group");
 };
 
 // The tile that also computes remainder strips (64 x 64, 32-deep panels, 4
@@ -471,7 +476,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     // to their fragment reads and MFMAs instead of queueing behind the loads
     // (+3.6 % at 2048^3, +1.4 % at 8192^3; 4 or 12 loaders, or the last 8 or
     // every other wave as loaders, were slower).
-    constexpr int NL = T::kLoaders;
+    // With a loader wave (LW) that wave issues every load instruction of a
+    // panel and the group's waves issue none.
+    constexpr bool LW = T::kLoaderWave;
+    constexpr int NL = LW ? 1 : T::kLoaders;
     constexpr int kInstA = kA / kSpanA, kInstB = kB / kSpanB;
     constexpr int kLoadsA = (kInstA + NL - 1) / NL;   // instructions per loader wave per panel
     constexpr int kLoadsB = (kInstB + NL - 1) / NL;
@@ -504,7 +512,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     const int lh = lane / 32;
 
     // Slot -> source element maps, fixed for the whole kernel (loader waves).
-    const bool loader = gw < NL;
+    const bool loader = !LW && gw < NL;
     const int lw = loader ? gw : 0;
     uint32_t a_off[kLoadsA];     // byte offset from the panel's (m0, k0) corner
     int a_r[kLoadsA], a_k[kLoadsA];
@@ -722,7 +730,8 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             //    each read is issued between two MFMAs of the k-group before.
             //  - The panel loads of round it+1 are spread through the MFMAs
             //    of round it, one load every kGap MFMAs from the first
-            //    k-groups on, into the buffer round it-1 used.
+            //    k-groups on, into the buffer round it-1 used (with loader
+            //    waves, those waves issue them and the MFMA waves none).
             //  - One barrier per round, halfway through the last k-group: the
             //    wave's own loads have landed (vmcnt), all waves are done
             //    with the buffer of round it (their last reads fed the MFMAs
@@ -757,10 +766,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             // with a single group (KS == 1) may use it: K-split groups can
             // have different round counts, and one-wave groups (NW == 1)
             // therefore run their rounds without any barrier.
-            static_assert((KS == 1 || NW == 1) && S == 2 && Q % 2 == 0 && NL == NW && kEvenA && kEvenB,
-                          "pipelined rounds: one group of all-loading waves, or one-wave groups; two buffers; "
-                          "even k-group count");
-            static_assert(kPerBlock >= 1 && (kLoads + kPerBlock - 1) / kPerBlock <= Q - 1,
+            static_assert((KS == 1 || NW == 1) && S == 2 && Q % 2 == 0 && (LW || (NL == NW && kEvenA && kEvenB)),
+                          "pipelined rounds: one group of all-loading waves (or a loader wave), or one-wave "
+                          "groups; two buffers; even k-group count");
+            static_assert(LW || (kPerBlock >= 1 && (kLoads + kPerBlock - 1) / kPerBlock <= Q - 1),
                           "the panel loads fit in the k-groups before the barrier");
             uint32_t oa_t[kLoadsA], ob_t[kLoadsB];
 #pragma unroll
@@ -822,15 +831,81 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 if constexpr (NW > 1)
                     __syncthreads();
             };
-            if (my_rounds > 0) {
-            {
+            // Loader waves (LW): they issue every load of a panel, in the
+            // group's round structure -- round it+1 goes into the idle
+            // buffer right after round it-1's barrier; each loader waits for
+            // its loads and meets the MFMA waves at round it's barrier (and
+            // at the tail clearing's).  The panel's load instructions (A's,
+            // then B's) are dealt to the loader waves in equal runs.
+            if (LW && gw >= NW) {
+                constexpr int NLW = LW ? T::kLoaderWaves : 1;
+                constexpr int kPer = (kInstA + kInstB) / NLW;
+                static_assert((kInstA + kInstB) % NLW == 0, "equal loader shares");
+                auto loader_rounds = [&](auto lv_c) {
+                    constexpr int lv = decltype(lv_c)::value;
+                    uint32_t off[kPer];
+#pragma unroll
+                    for (int j = 0; j < kPer; ++j) {
+                        const int x = lv * kPer + j;
+                        if (x < kInstA) {
+                            const int f = x * kSpanA + lane * kVecA;
+                            const int r = f / BK, e = f % BK;
+                            const int k = 4 * ((e / 4) ^ swz_a<BK>(r)) + e % 4;
+                            off[j] = m0 + r < g.M ? (uint32_t)(r * g.lda + k) * 4u : kOutOfRange;
+                        } else {
+                            const int f = (x - kInstA) * kSpanB + lane * kVecB;
+                            const int k = kNarrowB ? (f / BN) ^ ((f / BN >> 2) & 1) : f / BN;
+                            const int c = kNarrowB ? f % BN : (f % BN) ^ (((k >> 2) & 1) * 32);
+                            off[j] = n0 + c < g.N ? (uint32_t)(k * g.ldb + c) * 4u : kOutOfRange;
+                        }
+                    }
+                    auto slot = [](int x) { return x < kInstA ? x * kSpanA : kA + (x - kInstA) * kSpanB; };
+                    auto issue = [&](int buf, const Rsrc &r) {
+                        if constexpr (kPoisonLds) {
+#pragma unroll
+                            for (int j = 0; j < kPer; ++j)
+                                poison16(&stage[buf][slot(lv * kPer + j) + lane * 4]);
+                            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        }
+                        // vmcnt counts at most 63 loads in flight: past
+                        // that, each load waits for the oldest to land.
+#pragma unroll
+                        for (int j = 0; j < kPer; ++j) {
+                            const int x = lv * kPer + j;
+                            if (j >= 63)
+                                asm volatile("s_waitcnt vmcnt(62)" ::: "memory");
+                            buffer_to_lds(x < kInstA ? r.a : r.b, &stage[buf][slot(x)], off[j]);
+                        }
+                    };
+                    issue(0, rsrc(panel_k(0), true));
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    __builtin_amdgcn_s_barrier();
+                    if (cols_tail && tail_round == 0)
+                        group_sync();
+                    for (int it = 0; it < my_rounds; ++it) {
+                        issue((it & 1) ^ 1, rsrc(panel_k(it + 1), it + 1 < my_rounds));
+                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        __builtin_amdgcn_s_barrier();
+                        if (cols_tail && it + 1 == tail_round)
+                            group_sync();
+                    }
+                };
+                if (my_rounds > 0) {
+                    if (gw == NW)
+                        loader_rounds(std::integral_constant<int, 0>{});
+                    else if constexpr (NLW > 1)
+                        loader_rounds(std::integral_constant<int, 1>{});
+                    static_assert(NLW <= 2, "one or two loader waves");
+                }
+            } else if (my_rounds > 0) {
+            if constexpr (!LW) {
                 const Rsrc r0 = rsrc(panel_k(0), true);
                 poison_loads(0);
 #pragma unroll
                 for (int x = 0; x < kLoads; ++x)
                     load_one(0, r0, x);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             if constexpr (NW > 1)
                 __builtin_amdgcn_s_barrier();
             if (cols_tail && tail_round == 0) {
@@ -841,34 +916,44 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             read_frag(F[0], 0, 0);
             for (int it = 0; it < my_rounds; ++it) {
                 const int buf = it & 1;
-                const Rsrc nx = rsrc(panel_k(it + 1), it + 1 < my_rounds);
-                poison_loads(buf ^ 1);
+                Rsrc nx;
+                if constexpr (!LW) {
+                    nx = rsrc(panel_k(it + 1), it + 1 < my_rounds);
+                    poison_loads(buf ^ 1);
+                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int q = 0; q + 1 < Q; ++q) {
                     read_frag(F[(q + 1) & 1], buf, q + 1);
+                    if constexpr (!LW) {
 #pragma unroll
-                    for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
-                        if (x < kLoads)
-                            load_one(buf ^ 1, nx, x);
+                        for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
+                            if (x < kLoads)
+                                load_one(buf ^ 1, nx, x);
+                    }
                     mma(F[q & 1]);
 #pragma unroll
                     for (int r = 0; r < kReads; ++r) {
                         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
+                    if constexpr (!LW) {
 #pragma unroll
-                    for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
-                        if (x < kLoads) {
-                            __builtin_amdgcn_sched_group_barrier(0x008, kGap, 0);
-                            __builtin_amdgcn_sched_group_barrier(0x060, 1, 0);
-                        }
+                        for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
+                            if (x < kLoads) {
+                                __builtin_amdgcn_sched_group_barrier(0x008, kGap, 0);
+                                __builtin_amdgcn_sched_group_barrier(0x060, 1, 0);
+                            }
+                    }
                     __builtin_amdgcn_sched_group_barrier(0x008, kMfma, 0);
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 mma_part(F[(Q - 1) & 1], 0, 2);
                 __builtin_amdgcn_sched_barrier(0);
-                asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+                if constexpr (LW)
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                else
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
                 if constexpr (NW > 1)
                     __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
@@ -1047,7 +1132,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 }
                 return;
             }
-            if (group == 0) {
+            if (group == 0 && gw < NW) {    // not the loader wave
 #pragma unroll
                 for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -1372,16 +1457,20 @@ using Tile128x64K32 = MfmaTile<128, 64, 32, 2, 2>;
 using Tile64x64K64 = MfmaTile<64, 64, 64, 2, 2>;         // 64-deep panels
 // 2 K-split groups of 8 waves of 32 x 64, 4 of them loading
 using Tile128x128K32S2 = MfmaTile<128, 128, 32, 4, 2, 2, 2, 8, 4>;
-// Software-pipelined 4-wave tiles: 4 waves of 128 x 128, and of 64 x 64
+// Software-pipelined 4-wave tiles: 4 waves of 128 x 128, and 4 waves of
+// 64 x 64 on 64-deep panels (128 KiB of LDS) with two more waves that issue
+// every panel load (the MFMA waves only read LDS: 2048^3 in 123.0 us against
+// 125.6 when the four MFMA waves also load; 2372 x 1619 x 7588: 437 against
+// 449; stream-K over 5000 x 2600 x 4096: 792 against 811).  One loader wave
+// needs 64 loads per panel, past the 63 vmcnt can count (124.1 us).
 using Tile256x256K32P = MfmaTile<256, 256, 32, 2, 2, 1, 2, 8, 0, 1>;
-using Tile128x128K64P = MfmaTile<128, 128, 64, 2, 2, 1, 2, 8, 0, 1>;
+using Tile128x128K64PL2 = MfmaTile<128, 128, 64, 2, 2, 1, 2, 8, 0, 1, 2>;
 // Software-pipelined K-split: 8 one-wave groups, each with the whole 64 x 64
 // tile for every 8th 16-deep panel
 using Tile64x64K16S8P = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
 // Software-pipelined 4 waves of 64 x 64 on 16-deep panels (32 KiB of LDS,
 // three workgroups per CU)
 using Tile128x128K16P = MfmaTile<128, 128, 16, 2, 2, 1, 2, 8, 0, 1>;
-
 // Software-pipelined 4 waves of 64 x 64 on 32-deep panels (64 KiB of LDS,
 // two workgroups per CU)
 using Tile128x128K32P = MfmaTile<128, 128, 32, 2, 2, 1, 2, 8, 0, 1>;
@@ -1562,8 +1651,8 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile128x128K32S2>("dma_128x128x32_ksplit2"),
     config_dma<Tile256x256K32P, true>("dma_256x256x32_pipe"),
     config_streamk<Tile256x256K32P, true>("dma_256x256x32_pipe_sk"),
-    config_dma<Tile128x128K64P, true>("dma_128x128x64_pipe"),
-    config_streamk<Tile128x128K64P, true>("dma_128x128x64_pipe_sk"),
+    config_dma<Tile128x128K64PL2, true>("dma_128x128x64_pipe_lw2"),
+    config_streamk<Tile128x128K64PL2, true>("dma_128x128x64_pipe_lw2_sk"),
     config_dma<Tile64x64K16S8P, true>("dma_64x64x16_ksplit8_pipe"),
     config_streamk<Tile64x64K32S4>("dma_64x64x32_ksplit4_sk"),
     config_dma<Tile128x128K16P, true>("dma_128x128x16_pipe"),

@@ -126,8 +126,8 @@ def test_describe():
 
 
 WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
-              "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
-              "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe",
+              "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe_lw2",
+              "dma_128x128x64_pipe_lw2_sk", "dma_64x64x16_ksplit8_pipe",
               "dma_128x128x16_pipe", "dma_128x128x32_pipe"]
 
 
@@ -187,7 +187,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
 
 
 @pytest.mark.parametrize("shape,name", [
-    ((8192, 8192, 8192), "dma_256x256x32_pipe "), ((2048, 2048, 2048), "dma_128x128x64_pipe "),
+    ((8192, 8192, 8192), "dma_256x256x32_pipe "), ((2048, 2048, 2048), "dma_128x128x64_pipe_lw2 "),
     ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x32_pipe "),
     ((8192, 8192, 128), "dma_128x128x16_pipe "), ((8192, 8192, 512), "dma_128x128x16_pipe "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
@@ -221,23 +221,23 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # three rounds and more: 4-wave 64 x 64 tiles, several per CU
     ((3072, 1024, 2048), "dma_64x64x32 "), ((2176, 2100, 1000), "dma_64x64x32 "),
     # 400, 576 and 576 128 x 128 tiles, K >= 2048: stream-K over them
-    ((2560, 2560, 2560), "dma_128x128x64_pipe_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_sk "),
+    ((2560, 2560, 2560), "dma_128x128x64_pipe_lw2_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_lw2_sk "),
     ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "),
     # two or more balanced rounds of 128 x 128 tiles: 16-deep pipelined
     # panels for K < 2048
     ((6000, 2000, 1000), "dma_128x128x16_pipe "), ((4096, 3072, 1024), "dma_128x128x16_pipe "),
     ((4096, 2048, 2048), "dma_128x128x32_pipe "), ((4096, 2048, 1024), "dma_128x128x32_pipe "),
-    ((6144, 2048, 4096), "dma_128x128x16_pipe "), ((2048, 2048, 1024), "dma_128x128x64_pipe "),
+    ((6144, 2048, 4096), "dma_128x128x16_pipe "), ((2048, 2048, 1024), "dma_128x128x64_pipe_lw2 "),
     # a side of at most 64 (or 129 to 192): 128-wide tiles would be mostly
     # padding, so only the 64 x 64 choices; a side of 96 or 128 keeps them
     ((64, 32768, 4096), "dma_64x64x16_ksplit8_pipe "), ((32768, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
     ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x64 "),
     ((64, 65536, 1024), "dma_64x128x32 "), ((65536, 64, 1024), "dma_128x64x32 "),
-    ((96, 32768, 4096), "dma_128x128x64_pipe "), ((128, 32768, 4096), "dma_128x128x64_pipe "),
+    ((96, 32768, 4096), "dma_128x128x64_pipe_lw2 "), ((128, 32768, 4096), "dma_128x128x64_pipe_lw2 "),
     # a second round exactly half full (384 tiles): stream-K over the K split
     ((64, 24576, 4096), "dma_64x64x32_ksplit4_sk "), ((128, 12288, 12000), "dma_64x64x32_ksplit4_sk "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
-    ((1792, 1792, 1792), "dma_128x128x64_pipe "),
+    ((1792, 1792, 1792), "dma_128x128x64_pipe_lw2 "),
 ])
 def test_selection(shape, name):
     M, N, K = shape

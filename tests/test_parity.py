@@ -210,8 +210,8 @@ def test_unaligned_bases(dev, config):
 
 
 WRITE_BACK = ["dma_64x64x32", "dma_64x128x32", "dma_128x64x32", "dma_64x64x32_sk",
-              "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe",
-              "dma_128x128x64_pipe_sk", "dma_64x64x16_ksplit8_pipe",
+              "dma_256x256x32_pipe", "dma_256x256x32_pipe_sk", "dma_128x128x64_pipe_lw2",
+              "dma_128x128x64_pipe_lw2_sk", "dma_64x64x16_ksplit8_pipe",
               "dma_128x128x16_pipe", "dma_128x128x32_pipe"]
 
 
@@ -328,7 +328,7 @@ def test_graph_capture_replays_match_eager(dev):
         assert torch.equal(zout, torch.zeros_like(zout))
 
 
-GRAPH_PLANS = [((2048, 2048, 512), "dma_128x128x64_pipe "), ((4096, 4096, 128), "dma_128x128x16_pipe "),
+GRAPH_PLANS = [((2048, 2048, 512), "dma_128x128x64_pipe_lw2 "), ((4096, 4096, 128), "dma_128x128x16_pipe "),
                ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
                ((512, 512, 512), "dma_32x32x32_ksplit8 "), ((640, 640, 2048), "dma_32x64x16_ksplit8 ")]
 
@@ -422,7 +422,7 @@ def test_random_shapes_layouts_and_configs(dev):
 STREAMK = [("dma_64x64x32_ksplit4_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
            ("dma_64x64x64_sk", (1100, 1050, 200)),
            ("dma_64x64x64_sk", (1025, 1023, 1000)),
-           ("dma_128x128x32_w16_sk", (2176, 2100, 1000)), ("dma_128x128x64_pipe_sk", (2176, 2100, 1003)),
+           ("dma_128x128x32_w16_sk", (2176, 2100, 1000)), ("dma_128x128x64_pipe_lw2_sk", (2176, 2100, 1003)),
            ("dma_256x256x32_pipe_sk", (4352, 4200, 203)), ("dma_256x256x32_pipe_sk", (4352, 4200, 200))]
 
 
