@@ -491,7 +491,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     // It pays where writing C weighs most, the 4-wave tiles chosen for short
     // K; on the 16-wave tiles of long-K problems it measured 0.4-0.8 % slower.
     constexpr bool kBandEpilogue = KS == 1 && NW == 4 && BN >= 64 && T::kWaveM * BN <= S * kStage;
-    static_assert(S >= 2 && (S - 2) * kLoads <= 63, "vmcnt range");
+    static_assert(S >= 2 && (LW || (S - 2) * kLoads <= 63), "vmcnt range");
     static_assert(S == 2 || (kEvenA && kEvenB), "partial vmcnt waits need equal per-wave load counts");
     static_assert(KS * S * kStage * 4 <= 160 * 1024, "LDS budget");
     static_assert(KS == 1 || KS * S * kStage >= BM * BN, "the K-split reduction reuses the panel buffers");
@@ -766,9 +766,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             // with a single group (KS == 1) may use it: K-split groups can
             // have different round counts, and one-wave groups (NW == 1)
             // therefore run their rounds without any barrier.
-            static_assert((KS == 1 || NW == 1) && S == 2 && Q % 2 == 0 && (LW || (NL == NW && kEvenA && kEvenB)),
-                          "pipelined rounds: one group of all-loading waves (or a loader wave), or one-wave "
-                          "groups; two buffers; even k-group count");
+            static_assert((KS == 1 || NW == 1) && (S == 2 || LW) && Q % 2 == 0 &&
+                              (LW || (NL == NW && kEvenA && kEvenB)),
+                          "pipelined rounds: one group of all-loading waves (or loader waves), or one-wave "
+                          "groups; two buffers (a deeper ring with loader waves); even k-group count");
             static_assert(LW || (kPerBlock >= 1 && (kLoads + kPerBlock - 1) / kPerBlock <= Q - 1),
                           "the panel loads fit in the k-groups before the barrier");
             uint32_t oa_t[kLoadsA], ob_t[kLoadsB];
@@ -832,15 +833,19 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     __syncthreads();
             };
             // Loader waves (LW): they issue every load of a panel, in the
-            // group's round structure -- round it+1 goes into the idle
-            // buffer right after round it-1's barrier; each loader waits for
-            // its loads and meets the MFMA waves at round it's barrier (and
-            // at the tail clearing's).  The panel's load instructions (A's,
-            // then B's) are dealt to the loader waves in equal runs.
+            // group's round structure -- with a ring of S buffers, round
+            // it+S-1 goes into the buffer round it-1 used right after round
+            // it-1's barrier; each loader waits until its loads of round
+            // it+1 have landed and meets the MFMA waves at round it's barrier
+            // (and at the tail clearing's).  The MFMA waves' side of the
+            // loop is the same as without loader waves, minus the loads.
+            // The panel's load instructions (A's, then B's) are dealt to the
+            // loader waves in equal runs.
             if (LW && gw >= NW) {
                 constexpr int NLW = LW ? T::kLoaderWaves : 1;
                 constexpr int kPer = (kInstA + kInstB) / NLW;
                 static_assert((kInstA + kInstB) % NLW == 0, "equal loader shares");
+                static_assert(S == 2 || (S - 1) * kPer <= 63, "a deeper ring keeps its rounds' loads within vmcnt");
                 auto loader_rounds = [&](auto lv_c) {
                     constexpr int lv = decltype(lv_c)::value;
                     uint32_t off[kPer];
@@ -877,14 +882,20 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                             buffer_to_lds(x < kInstA ? r.a : r.b, &stage[buf][slot(x)], off[j]);
                         }
                     };
-                    issue(0, rsrc(panel_k(0), true));
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                    // Rounds 0 .. S-2 first; then, after round it-1's
+                    // barrier, round it+S-1 into the buffer round it-1
+                    // used.  Before round it's barrier round it+1 must have
+                    // landed: the S-2 rounds after it may still be in flight.
+#pragma unroll
+                    for (int r = 0; r + 1 < S; ++r)
+                        issue(r, rsrc(panel_k(r), r < my_rounds));
+                    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPer) : "memory");
                     __builtin_amdgcn_s_barrier();
                     if (cols_tail && tail_round == 0)
                         group_sync();
                     for (int it = 0; it < my_rounds; ++it) {
-                        issue((it & 1) ^ 1, rsrc(panel_k(it + 1), it + 1 < my_rounds));
-                        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                        issue((it + S - 1) % S, rsrc(panel_k(it + S - 1), it + S - 1 < my_rounds));
+                        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPer) : "memory");
                         __builtin_amdgcn_s_barrier();
                         if (cols_tail && it + 1 == tail_round)
                             group_sync();
@@ -915,11 +926,11 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             Frag F[2];
             read_frag(F[0], 0, 0);
             for (int it = 0; it < my_rounds; ++it) {
-                const int buf = it & 1;
+                const int buf = it % S, nbuf = (it + 1) % S;
                 Rsrc nx;
                 if constexpr (!LW) {
                     nx = rsrc(panel_k(it + 1), it + 1 < my_rounds);
-                    poison_loads(buf ^ 1);
+                    poison_loads(nbuf);
                 }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -929,7 +940,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
 #pragma unroll
                         for (int x = q * kPerBlock; x < (q + 1) * kPerBlock; ++x)
                             if (x < kLoads)
-                                load_one(buf ^ 1, nx, x);
+                                load_one(nbuf, nx, x);
                     }
                     mma(F[q & 1]);
 #pragma unroll
@@ -958,10 +969,10 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     __builtin_amdgcn_s_barrier();
                 __builtin_amdgcn_sched_barrier(0);
                 if (cols_tail && it + 1 == tail_round) {
-                    clear_cols(buf ^ 1);
+                    clear_cols(nbuf);
                     group_sync();
                 }
-                read_frag(F[0], buf ^ 1, 0);
+                read_frag(F[0], nbuf, 0);
                 mma_part(F[(Q - 1) & 1], 2, 4);
 #pragma unroll
                 for (int r = 0; r < kReads; ++r) {
@@ -1465,6 +1476,9 @@ using Tile128x128K32S2 = MfmaTile<128, 128, 32, 4, 2, 2, 2, 8, 4>;
 // needs 64 loads per panel, past the 63 vmcnt can count (124.1 us).
 using Tile256x256K32P = MfmaTile<256, 256, 32, 2, 2, 1, 2, 8, 0, 1>;
 using Tile128x128K64PL2 = MfmaTile<128, 128, 64, 2, 2, 1, 2, 8, 0, 1, 2>;
+// 4 waves of 32 x 32 fed by two loader waves through a ring of four 32-deep
+// panels (64 KiB of LDS): three rounds of loads in flight.
+using Tile64x64K32PL2S4 = MfmaTile<64, 64, 32, 2, 2, 1, 4, 8, 0, 1, 2>;
 // Software-pipelined K-split: 8 one-wave groups, each with the whole 64 x 64
 // tile for every 8th 16-deep panel
 using Tile64x64K16S8P = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
@@ -1513,6 +1527,7 @@ enum ConfigId {
     kCfgDma32x64K16S8,
     kCfgDma64x32K16S8,
     kCfgDma128x128K32P,
+    kCfgDma64x64K32PL2S4,
     kNumConfigs
 };
 
@@ -1661,6 +1676,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile32x64K16S8>("dma_32x64x16_ksplit8"),
     config_dma<Tile64x32K16S8>("dma_64x32x16_ksplit8"),
     config_dma<Tile128x128K32P, true>("dma_128x128x32_pipe"),
+    config_dma<Tile64x64K32PL2S4>("dma_64x64x32_pipe_lw2_s4"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1864,11 +1880,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     if (!thin && deep_ok && K > 512 && 4 * t128 >= 3 * CU &&
         (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * CU)))
         return kCfgDma128x128K64P;
-    // 64 x 64 tiles with K > 512, up to three rounds of them: K split
-    // inside the workgroup.  One tile per CU: 8 pipelined one-wave groups
-    // for K >= 2048, else 4 groups of 4 waves; a last round at most half full:
-    // stream-K over the 4-group tile; two rounds otherwise, with K >= 2048:
-    // the 8 pipelined groups.
+    // 64 x 64 tiles with K > 512, up to three rounds of them.  One tile per
+    // CU: 8 pipelined one-wave K-split groups for K >= 1536, below it 4
+    // pipelined waves of 32 x 32 fed by two loader waves through a ring of
+    // four 32-deep panels (1000^3: 24.1 us against 25.1 for 4 K-split
+    // groups of 4 waves; 1024 x 1024 x 1536: 29.3 for the 8 groups against
+    // 31.4; 1000 x 1000 x 768: 19.6 against 19.9); a last round at most half
+    // full: stream-K over the 4-group K-split tile; two rounds otherwise,
+    // with K >= 2048: the 8 pipelined groups.
     const int64_t t32 = tiles(kCfgDma64x64K32);
     // A last tile row of at most kMaxStripRows rows that alone takes the
     // tiles past one round: those rows become a strip computed with FMAs by
@@ -1893,7 +1912,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         return kCfgDma64x64K32S4;
     }
     if (K > 512 && t32 <= CU)
-        return K >= 2048 ? kCfgDma64x64K16S8P : kCfgDma64x64K32S4;
+        return K >= 1536 ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
     const int64_t last = t32 - (ceil_div(t32, CU) - 1) * CU;   // tiles in the last round
     // (Past 320 tiles only with K >= 1100: below it the K-split groups'
     // fold and stream-K's extra launch cost more than the idle CUs;

@@ -191,11 +191,13 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((4096, 4096, 16384), "dma_256x256x32_pipe "), ((1024, 8192, 8192), "dma_128x128x32_pipe "),
     ((8192, 8192, 128), "dma_128x128x16_pipe "), ((8192, 8192, 512), "dma_128x128x16_pipe "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
-    # at most one 64 x 64 tile per CU: K split inside the workgroup, 8
-    # pipelined one-wave groups from K = 2048 on
+    # at most one 64 x 64 tile per CU: 8 pipelined one-wave K-split groups
+    # from K = 1536 on, below it 4 waves fed by two loader waves
     ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 16384, 4096), "dma_64x64x16_ksplit8_pipe "),
     ((1024, 1024, 8192), "dma_64x64x16_ksplit8_pipe "), ((100, 5000, 3000), "dma_64x64x16_ksplit8_pipe "),
-    ((1000, 1000, 1000), "dma_64x64x32_ksplit4 "), ((768, 768, 1024), "dma_64x64x32_ksplit4 "),
+    ((1024, 1024, 1536), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 1535), "dma_64x64x32_pipe_lw2_s4 "),
+    ((1000, 1000, 1000), "dma_64x64x32_pipe_lw2_s4 "), ((768, 768, 1024), "dma_64x64x32_pipe_lw2_s4 "),
+    ((1000, 1000, 513), "dma_64x64x32_pipe_lw2_s4 "),
     # K <= 512: no K split
     ((1000, 1000, 300), "dma_64x64x64 "),
     # few output tiles: 32 x 32 tiles of one-wave K-split groups while they
