@@ -169,6 +169,49 @@ def test_ragged_bit_exact(dev, shape, config):
     assert_bit_exact(got, oracle.gemm(A, B), f"{shape} config {config}")
 
 
+# ---------------------------------------------------------------------------
+# IEEE special values.  Whether an element of C is NaN, +Inf, -Inf or finite
+# does not depend on the order of its sum: a NaN product (NaN, or Inf times
+# zero) or +Inf meeting -Inf gives NaN, otherwise an infinite product decides
+# the sign, and the finite operands here are too small to overflow.  So every
+# configuration must classify each element of C exactly as the oracle does
+# (and agree with it within tolerance where C is finite), including the
+# elements fed by zero-filled or cleared padding.
+# ---------------------------------------------------------------------------
+SPECIAL_SHAPES = [(131, 97, 70), (300, 257, 1001)]
+
+
+def special_operands(M, N, K, count=None):
+    """Uniform operands with seeded NaN, +-Inf and +0 entries (about one in
+    2000, or `count` per operand), and one forced Inf x 0 product."""
+    A, B = (x.copy() for x in inputs.uniform(M, N, K))
+    rng = np.random.default_rng(M * 1000003 + N * 1009 + K)
+    specials = np.array([np.nan, np.inf, -np.inf, 0.0], dtype=np.float32)
+    for X in (A, B):
+        at = rng.choice(X.size, size=count or max(4, X.size // 2000), replace=False)
+        X.flat[at] = rng.choice(specials, size=at.size)
+    A[M // 2, K - 1] = np.inf
+    B[K - 1, N // 3] = 0.0
+    return A, B
+
+
+@pytest.mark.parametrize("config", CONFIGS, ids=CONFIG_IDS)
+@pytest.mark.parametrize("shape", SPECIAL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_special_values_classified_as_the_oracle(dev, shape, config):
+    M, N, K = shape
+    A, B = special_operands(M, N, K)
+    got, _ = gpu_gemm(A, B, config, dev)
+    with np.errstate(invalid="ignore"):
+        ref = oracle.gemm(A, B)
+    kinds = {"nan": np.isnan, "+inf": np.isposinf, "-inf": np.isneginf}
+    for name, f in kinds.items():
+        bad = np.flatnonzero(f(got) != f(ref))
+        assert bad.size == 0, f"{shape} config {config}: {bad.size} elements differ in being {name}; first {bad[0]}"
+    assert all(f(ref).any() for f in kinds.values()), "the operands should produce every kind"
+    fin = np.isfinite(ref)
+    assert_close(got[fin], ref[fin], f"special {shape} finite part")
+
+
 @pytest.mark.parametrize("config", CONFIGS, ids=CONFIG_IDS)
 def test_permutation_pins_lane_layout(dev, config):
     """X @ P and P @ Y are exact permutations: any lane/register mix-up in
@@ -607,6 +650,21 @@ def test_split_k_uniform_within_tolerance_and_deterministic(dev):
     for _ in range(2):
         again, _, _, _ = gpu_gemm_ws(A, B, dev)
         assert_bit_exact(again, first, "split-K repeat")
+
+
+def test_split_k_special_values_classified_as_the_oracle(dev):
+    """The slices' partial products and their ordered sum keep NaN and
+    +-Inf where the oracle has them."""
+    A, B = special_operands(200, 200, 20000, count=12)
+    got, _, _, need = gpu_gemm_ws(A, B, dev)
+    assert need > 0
+    with np.errstate(invalid="ignore"):
+        ref = oracle.gemm(A, B)
+    for f in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(f(got), f(ref)), f.__name__
+    fin = np.isfinite(ref)
+    assert fin.any() and not fin.all()
+    assert_close(got[fin], ref[fin], "split-K special finite part")
 
 
 def test_split_k_short_workspace_runs_the_plain_path(dev):
