@@ -1740,25 +1740,28 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    7.31 ms against 7.45 for 16 waves of 64 x 64; 4096 x 4096 x 16384: 3.66
 //    against 3.72); their stream-K twin for K >= 3072 if 128 x 128 tiles
 //    would not fill their rounds either (5000^3: 1832 us against 2381);
-//  * at least one 128 x 128 tile per CU: 128 x 128 with 4 pipelined waves
-//    of 64 x 64, 64-deep panels (2048^3: 125 us against 133 for 16 waves in
-//    two K-split groups); with two or more balanced rounds and K < 2048, or
-//    eight and more rounds, 16-deep panels and three workgroups per CU
-//    instead (4096 x 3072 x 1024: 185 us against 193; but 4096 x 2048 x
-//    2048: 250 against 247); their stream-K twin when the rounds are not
-//    filled, for K >= 2048 or K >= 1024 with two or more tiles per CU
-//    (3072^3: 428 us against 455 for 64 x 64); otherwise, and for one or two
-//    rounds with K < 512, 64 x 64 tiles;
+//  * at least one 128 x 128 tile per CU, rounds filled: 128 x 128 with 4
+//    pipelined waves of 64 x 64 -- one round: 64-deep panels fed by two
+//    loader waves (2048^3: 123 us against 125.6 when the MFMA waves load,
+//    133 for 16 waves in two K-split groups); two rounds: 32-deep panels,
+//    two workgroups per CU (4096 x 2048 x 2048: 243 us against 248); more:
+//    16-deep panels, three workgroups per CU (6144 x 2048 x 4096: 717
+//    against 727); rounds not filled: the loader-wave tile's stream-K twin
+//    for K >= 2048, or K >= 1024 with two or more tiles per CU (3072^3: 428
+//    us against 455 for 64 x 64); otherwise, and for one or two rounds with
+//    K < 512, 64 x 64 tiles;
 //  * at least three quarters of the CUs busy with 128 x 128 tiles while
 //    64 x 64 tiles would leave the last round mostly idle, or four fifths
-//    busy with K >= 2048: one round of the pipelined 128 x 128 tile (1792^3:
-//    110 us against 121 for 64 x 64);
+//    busy with K >= 2048: one round of the loader-wave 128 x 128 tile
+//    (1792^3: 109 us against 121 for 64 x 64);
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
-//    shapes): 64 x 64 with K split over wave groups inside the workgroup.
-//    For K >= 2048, 8 software-pipelined one-wave groups (16384 x 64 x 4096:
-//    72 us against 79 for 4 groups of 4 waves; 1024 x 1024 x 8192: 130
-//    against 149), below that 4 groups of 4 waves (1024^3: 25.4 us against
-//    26.3 for the 8 groups and 26.7 for 4 waves on 64-deep panels);
+//    shapes): for K >= 1536, K split over 8 software-pipelined one-wave
+//    groups (16384 x 64 x 4096: 72 us against 79 for 4 groups of 4 waves;
+//    1024 x 1024 x 1536: 29.3 against 31.4), below that 4 pipelined waves of
+//    32 x 32 fed by two loader waves through four 32-deep panels (1000^3:
+//    24.1 us against 25.1 for 4 K-split groups of 4 waves); a last tile row
+//    (column) of 1-4 rows (columns) past one round: one round of the 4-group
+//    K-split tile, the remainder computed as a strip;
 //  * up to three rounds of 64 x 64 tiles with a last round at most half full:
 //    stream-K over the 4-group K-split tile, past 320 tiles only with K >=
 //    1100 (1200 x 1200 x 4096: 120 us against 149 for 64 x 64; 1536^3: 81
