@@ -782,16 +782,29 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             struct Rsrc {
                 __amdgpu_buffer_rsrc_t a, b;
             };
-            auto rsrc = [&](int k0, bool on) {
-                const bool last = k0 + BK > g.K;
-                const int64_t a_end = 4 * ((int64_t)(g.M - 1 - m0) * g.lda + (g.K - k0));
-                const int ar = !on ? 0 : (last && a_end < (int64_t)kOutOfRange) ? (int)a_end : (int)kOutOfRange;
-                const int br = !on ? 0 : last ? 4 * ((g.K - 1 - k0) * (int)g.ldb + (g.N - n0)) : (int)kOutOfRange;
-                return Rsrc{__builtin_amdgcn_make_buffer_rsrc((void *)(g.A + ((int64_t)m0 * g.lda + k0)), 0, ar,
-                                                              kRawBufferFlags),
-                            __builtin_amdgcn_make_buffer_rsrc((void *)(g.B + ((int64_t)k0 * g.ldb + n0)), 0, br,
-                                                              kRawBufferFlags)};
+            // This group's rounds: panels p_begin + group, + KS, ... below
+            // p_end; the panel holding column K-1 is its round tail_round if
+            // the group is tail_group.
+            const int my_rounds = npanels > group ? (npanels - group + KS - 1) / KS : 0;
+            const bool cols_tail = g.K % BK != 0 && p_end == ktiles && group == tail_group;
+            // The ranges of the panel holding column K-1, worked out once:
+            // per round only selects and the panel's base addresses remain,
+            // with no branch (so that they can sit between MFMAs).
+            const int k_last = (ktiles - 1) * BK;
+            const int64_t a_end = 4 * ((int64_t)(g.M - 1 - m0) * g.lda + (g.K - k_last));
+            const int ar_last = a_end < (int64_t)kOutOfRange ? (int)a_end : (int)kOutOfRange;
+            const int br_last = 4 * ((g.K - 1 - k_last) * (int)g.ldb + (g.N - n0));
+            // Round it's panels start at a_at(it) and b_at(it).
+            auto a_at = [&](int it) { return g.A + ((int64_t)m0 * g.lda + panel_k(it)); };
+            auto b_at = [&](int it) { return g.B + ((int64_t)panel_k(it) * g.ldb + n0); };
+            auto rsrc_from = [&](const float *pa, const float *pb, int it) {
+                const bool on = it < my_rounds, last = cols_tail && it == tail_round;
+                const int ar = on ? (last ? ar_last : (int)kOutOfRange) : 0;
+                const int br = on ? (last ? br_last : (int)kOutOfRange) : 0;
+                return Rsrc{__builtin_amdgcn_make_buffer_rsrc((void *)pa, 0, ar, kRawBufferFlags),
+                            __builtin_amdgcn_make_buffer_rsrc((void *)pb, 0, br, kRawBufferFlags)};
             };
+            auto rsrc = [&](int it) { return rsrc_from(a_at(it), b_at(it), it); };
             // Load x of a wave's panel share (A's loads first, then B's).
             // Debug build: NaN into every slot this wave's loads of one
             // round fill, before they are issued.
@@ -812,11 +825,6 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 else
                     buffer_to_lds(r.b, &stage[buf][kA + (lw * kLoadsB + x - kLoadsA) * kSpanB], ob_t[x - kLoadsA]);
             };
-            // This group's rounds: panels p_begin + group, + KS, ... below
-            // p_end; the panel holding column K-1 is its round tail_round if
-            // the group is tail_group.
-            const int my_rounds = npanels > group ? (npanels - group + KS - 1) / KS : 0;
-            const bool cols_tail = g.K % BK != 0 && p_end == ktiles && group == tail_group;
             constexpr int NT = NW * kWaveSize;                   // threads of the group
             auto clear_cols = [&](int buf) {
                 const int valid = g.K - (ktiles - 1) * BK;
@@ -888,13 +896,13 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     // landed: the S-2 rounds after it may still be in flight.
 #pragma unroll
                     for (int r = 0; r + 1 < S; ++r)
-                        issue(r, rsrc(panel_k(r), r < my_rounds));
+                        issue(r, rsrc(r));
                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPer) : "memory");
                     __builtin_amdgcn_s_barrier();
                     if (cols_tail && tail_round == 0)
                         group_sync();
                     for (int it = 0; it < my_rounds; ++it) {
-                        issue((it + S - 1) % S, rsrc(panel_k(it + S - 1), it + S - 1 < my_rounds));
+                        issue((it + S - 1) % S, rsrc(it + S - 1));
                         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((S - 2) * kPer) : "memory");
                         __builtin_amdgcn_s_barrier();
                         if (cols_tail && it + 1 == tail_round)
@@ -910,7 +918,7 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                 }
             } else if (my_rounds > 0) {
             if constexpr (!LW) {
-                const Rsrc r0 = rsrc(panel_k(0), true);
+                const Rsrc r0 = rsrc(0);
                 poison_loads(0);
 #pragma unroll
                 for (int x = 0; x < kLoads; ++x)
@@ -925,13 +933,16 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             }
             Frag F[2];
             read_frag(F[0], 0, 0);
+            // Round it+1's panels, advanced by one round's step in round it.
+            const float *pa = a_at(1), *pb = b_at(1);
+            const int64_t step_b = (int64_t)KS * BK * g.ldb;
+            Rsrc nx;
+            if constexpr (!LW)
+                nx = rsrc_from(pa, pb, 1);
             for (int it = 0; it < my_rounds; ++it) {
                 const int buf = it % S, nbuf = (it + 1) % S;
-                Rsrc nx;
-                if constexpr (!LW) {
-                    nx = rsrc(panel_k(it + 1), it + 1 < my_rounds);
+                if constexpr (!LW)
                     poison_loads(nbuf);
-                }
                 __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int q = 0; q + 1 < Q; ++q) {
@@ -973,14 +984,28 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
                     group_sync();
                 }
                 read_frag(F[0], nbuf, 0);
+                // The next round's buffer descriptors, worked out here
+                // between MFMAs rather than ahead of the next round's first.
+                Rsrc nn;
+                if constexpr (!LW) {
+                    pa += KS * BK;
+                    pb += step_b;
+                    nn = rsrc_from(pa, pb, it + 2);
+                }
                 mma_part(F[(Q - 1) & 1], 2, 4);
 #pragma unroll
                 for (int r = 0; r < kReads; ++r) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, kMfma / 2, 0);
+#pragma unroll
+                for (int r = kReads; r < kMfma / 2; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x004, 2, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
+                if constexpr (!LW)
+                    nx = nn;
             }
             }
         } else {
