@@ -1780,19 +1780,21 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    busy with K >= 2048: one round of the loader-wave 128 x 128 tile
 //    (1792^3: 109 us against 121 for 64 x 64);
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
-//    shapes): for K >= 1536, K split over 8 software-pipelined one-wave
+//    shapes): from K = 640 on, K split over 8 software-pipelined one-wave
 //    groups (16384 x 64 x 4096: 72 us against 79 for 4 groups of 4 waves;
-//    1024 x 1024 x 1536: 29.3 against 31.4), below that 4 pipelined waves of
-//    32 x 32 fed by two loader waves through four 32-deep panels (1000^3:
-//    24.1 us against 25.1 for 4 K-split groups of 4 waves); a last tile row
+//    1024 x 1024 x 1280: 25.1 against 27.1 for the loader-wave tile), unless
+//    K < 1536 and its 16-deep panels split unevenly over the 8 groups; else
+//    4 pipelined waves of 32 x 32 fed by two loader waves through four
+//    32-deep panels (1000 x 1000 x 600: 17.6 us against 18.1); a last tile row
 //    (column) of 1-4 rows (columns) past one round: one round of the 4-group
 //    K-split tile, the remainder computed as a strip;
 //  * up to three rounds of 64 x 64 tiles with a last round at most half full:
 //    stream-K over the 4-group K-split tile, past 320 tiles only with K >=
 //    1100 (1200 x 1200 x 4096: 120 us against 149 for 64 x 64; 1536^3: 81
 //    against 83; (1025, 1023, 1000): 37.2 against 42.3); otherwise two
-//    rounds with K >= 2048, or three with K >= 4096: the 8 pipelined groups
-//    (1300 x 1300 x 4096: 136 us against 149);
+//    rounds with K >= 1024, or three with K >= 2048: the 8 pipelined groups
+//    (1300 x 1300 x 4096: 136 us against 149; 2048 x 1536 x 2048: 101
+//    against 110);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // Below the largest tile the choices use 32- or 64-deep K-panels: those
@@ -1909,13 +1911,17 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * CU)))
         return kCfgDma128x128K64P;
     // 64 x 64 tiles with K > 512, up to three rounds of them.  One tile per
-    // CU: 8 pipelined one-wave K-split groups for K >= 1536, below it 4
-    // pipelined waves of 32 x 32 fed by two loader waves through a ring of
-    // four 32-deep panels (1000^3: 24.1 us against 25.1 for 4 K-split
-    // groups of 4 waves; 1024 x 1024 x 1536: 29.3 for the 8 groups against
-    // 31.4; 1000 x 1000 x 768: 19.6 against 19.9); a last round at most half
-    // full: stream-K over the 4-group K-split tile; two rounds otherwise,
-    // with K >= 2048: the 8 pipelined groups.
+    // CU: 8 pipelined one-wave K-split groups from K = 640 on, unless the
+    // 16-deep panels split unevenly over the groups (the busiest group's
+    // rounds span over 9/8 of K rounded up to 32-deep panels) while K < 1536;
+    // otherwise 4 pipelined waves of 32 x 32 fed by two loader waves through
+    // a ring of four 32-deep panels (1024 x 1024 x 1280: 25.1 us for the 8
+    // groups against 27.1; 1000^3: 23.7 against 24.0, 25.1 for 4 K-split
+    // groups of 4 waves; 1024 x 1024 x 640: 16.0 against 17.2; but 800 x
+    // 1200 x 650, 41 panels over 8 groups: 18.8 against 18.3, and 1000 x
+    // 1000 x 600: 18.1 against 17.6); a last round at most half full:
+    // stream-K over the 4-group K-split tile; two rounds otherwise, with K >=
+    // 2048: the 8 pipelined groups.
     const int64_t t32 = tiles(kCfgDma64x64K32);
     // A last tile row of at most kMaxStripRows rows that alone takes the
     // tiles past one round: those rows become a strip computed with FMAs by
@@ -1939,8 +1945,11 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         strip_cols = N % 64;
         return kCfgDma64x64K32S4;
     }
-    if (K > 512 && t32 <= CU)
-        return K >= 1536 ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
+    if (K > 512 && t32 <= CU) {
+        const int64_t k8 = 128 * ceil_div(ceil_div(K, 16), 8);   // K the busiest of the 8 groups covers
+        const int64_t k4 = 32 * ceil_div(K, 32);                  // K the loader-wave tile covers
+        return K >= 1536 || (K >= 640 && 8 * k8 <= 9 * k4) ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
+    }
     const int64_t last = t32 - (ceil_div(t32, CU) - 1) * CU;   // tiles in the last round
     // (Past 320 tiles only with K >= 1100: below it the K-split groups'
     // fold and stream-K's extra launch cost more than the idle CUs;
@@ -1952,29 +1961,36 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     if (K > 512 && (K >= 1100 || t32 <= 5 * CU / 4) && t32 <= 3 * CU &&
         2 * last <= CU)
         return kCfgDma64x64K32S4SK;
-    if (K >= 2048 && t32 <= 2 * CU)
+    // Two rounds favour the 8 pipelined groups from K = 1024 on (2048 x
+    // 1024 x 1024: 39.3 us against 42.1 for 64 x 64 tiles of 4 waves; 1600
+    // x 1200 x 1200: 45.2 against 48.5; 2048 x 1024 x 1100: 45.5 against
+    // 45.3; but 1400 x 1400 x 1000: 43.6 against 42.3), three rounds with a
+    // fuller last one from K = 2048 on (2048 x 1536 x 2048: 101.2 against
+    // 109.5; 5932 x 460 x 2048: 101.7 against 109.4; but 1900 x 1600 x 1500:
+    // 83.2 against 81.7).
+    if (K >= 1024 && t32 <= 2 * CU)
         return kCfgDma64x64K16S8P;
-    // Three rounds with a fuller last one still favour the 8 pipelined
-    // groups once K is long (5932 x 460 x 4096: 200 us against 213 for
-    // 64 x 64 tiles of 4 waves; x 8192: 378 against 419; x 2048: 112
-    // against 110).
-    if (K >= 4096 && t32 <= 3 * CU)
+    if (K >= 2048 && t32 <= 3 * CU)
         return kCfgDma64x64K16S8P;
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
     if (tiles(wide) >= 2 * CU)
         return wide;
     // 64 x 64 tiles.  Up to two per CU, the one or two 4-wave workgroups
     // leave each SIMD one or two waves, and 64-deep panels halve the
-    // per-panel barrier stalls that then show; with more, several workgroups
-    // share a CU and the smaller 32-deep panels (more resident workgroups)
-    // win.
+    // per-panel barrier stalls that then show, unless their last panel is
+    // at most half used (K % 64 in 1..32), which 32-deep panels avoid
+    // (600 x 3000 x 200: 14.2 us against 15.6; 956 x 1597 x 331: 18.9
+    // against 20.1; but 1280 x 1280 x 512: 23.7 against 24.1 for 32-deep
+    // panels, 1000 x 1000 x 300: 12.6 against 12.8); with more, several
+    // workgroups share a CU and the smaller 32-deep panels (more resident
+    // workgroups) win.
     // Barely more than one tile per CU: stream-K, so the few extra tiles do
     // not double the time.
     const int64_t t64 = tiles(kCfgDma64x64K64);
     if (t64 > CU && 4 * t64 <= 5 * CU)
         return deep_ok ? kCfgDma64x64K64SK : kCfgDma64x64K32SK;
     if (t64 <= 2 * CU)
-        return deep_ok ? kCfgDma64x64K64 : kCfgDma64x64K32;
+        return deep_ok && 64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) ? kCfgDma64x64K64 : kCfgDma64x64K32;
     return kCfgDma64x64K32;
 }
 

@@ -169,7 +169,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # 63 rows of B span more than 2 GiB but 31 do not: the rule's 64-deep
     # choices give way to its 32-deep ones
     ldb = 10_000_000
-    rc, text = gb.gemm_f32_describe(-1, 2048, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
+    rc, text = gb.gemm_f32_describe(-1, 1400, 1400, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1400)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32 "), text
     rc, text = gb.gemm_f32_describe(-1, 2048, 2048, 2048, FAKE, 2048, FAKE, ldb, FAKE, 2048)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_ksplit2 "), text
@@ -192,14 +192,22 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((8192, 8192, 128), "dma_128x128x16_pipe "), ((8192, 8192, 512), "dma_128x128x16_pipe "),
     ((1, 1, 1), "valu"), ((15, 4000, 4000), "valu"),
     # at most one 64 x 64 tile per CU: 8 pipelined one-wave K-split groups
-    # from K = 1536 on, below it 4 waves fed by two loader waves
+    # from K = 640 on, unless below K = 1536 the 16-deep panels split
+    # unevenly over the groups (the busiest group's share of K rounded up
+    # over 9/8 of K rounded up to 32); otherwise 4 waves fed by two loader
+    # waves
     ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 16384, 4096), "dma_64x64x16_ksplit8_pipe "),
     ((1024, 1024, 8192), "dma_64x64x16_ksplit8_pipe "), ((100, 5000, 3000), "dma_64x64x16_ksplit8_pipe "),
-    ((1024, 1024, 1536), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 1535), "dma_64x64x32_pipe_lw2_s4 "),
-    ((1000, 1000, 1000), "dma_64x64x32_pipe_lw2_s4 "), ((768, 768, 1024), "dma_64x64x32_pipe_lw2_s4 "),
-    ((1000, 1000, 513), "dma_64x64x32_pipe_lw2_s4 "),
-    # K <= 512: no K split
-    ((1000, 1000, 300), "dma_64x64x64 "),
+    ((1024, 1024, 1536), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 1535), "dma_64x64x16_ksplit8_pipe "),
+    ((1000, 1000, 1000), "dma_64x64x16_ksplit8_pipe "), ((768, 768, 1024), "dma_64x64x16_ksplit8_pipe "),
+    ((1024, 1024, 640), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 700), "dma_64x64x16_ksplit8_pipe "),
+    ((800, 1200, 650), "dma_64x64x32_pipe_lw2_s4 "), ((1000, 1000, 639), "dma_64x64x32_pipe_lw2_s4 "),
+    ((1000, 1000, 600), "dma_64x64x32_pipe_lw2_s4 "), ((1000, 1000, 513), "dma_64x64x32_pipe_lw2_s4 "),
+    # K <= 512: no K split; 64-deep panels unless the last one would be at
+    # most half used (K % 64 in 1..32)
+    ((1000, 1000, 300), "dma_64x64x64 "), ((1280, 1280, 512), "dma_64x64x64 "),
+    ((600, 3000, 200), "dma_64x64x32 "), ((956, 1597, 331), "dma_64x64x32 "),
+    ((2712, 228, 94), "dma_64x64x32 "),
     # few output tiles: 32 x 32 tiles of one-wave K-split groups while they
     # fit one round (4 groups for K <= 256), then 32 x 64 or 64 x 32 ones
     ((512, 512, 512), "dma_32x32x32_ksplit8 "), ((512, 512, 1024), "dma_32x32x32_ksplit8 "),
@@ -213,15 +221,19 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1025, 1023, 2048), "dma_64x64x32_ksplit4_sk "), ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "),
     ((1023, 1025, 1000), "dma_64x64x32_ksplit4 "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
     # 272, 289, 324 and 576 64 x 64 tiles: the last round would be under
-    # half full; stream-K over the K-split tile.  400 tiles: 64 x 64 tiles
+    # half full; stream-K over the K-split tile.  400 tiles: two rounds of
+    # the pipelined K split
     ((1025, 1023, 3000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
     ((1100, 1100, 1100), "dma_64x64x32_ksplit4_sk "),
-    ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "), ((1280, 1280, 1280), "dma_64x64x64 "),
+    ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "), ((1280, 1280, 1280), "dma_64x64x16_ksplit8_pipe "),
     ((1025, 1023, 300), "dma_64x64x64_sk "),
-    # two balanced rounds: the pipelined K split for K >= 2048, else 64 x 64
-    ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe "), ((2048, 1024, 1024), "dma_64x64x64 "),
-    # three rounds and more: 4-wave 64 x 64 tiles, several per CU
-    ((3072, 1024, 2048), "dma_64x64x32 "), ((2176, 2100, 1000), "dma_64x64x32 "),
+    # two balanced rounds: the pipelined K split for K >= 1024, else 64 x 64
+    ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe "), ((2048, 1024, 1024), "dma_64x64x16_ksplit8_pipe "),
+    ((1400, 1400, 1000), "dma_64x64x64 "), ((2048, 1024, 768), "dma_64x64x64 "),
+    # three rounds: the pipelined K split for K >= 2048; more rounds: 4-wave
+    # 64 x 64 tiles, several per CU
+    ((3072, 1024, 2048), "dma_64x64x16_ksplit8_pipe "), ((1900, 1600, 1500), "dma_64x64x32 "),
+    ((2176, 2100, 1000), "dma_64x64x32 "),
     # 400, 576 and 576 128 x 128 tiles, K >= 2048: stream-K over them
     ((2560, 2560, 2560), "dma_128x128x64_pipe_lw2_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_lw2_sk "),
     ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "),
@@ -233,7 +245,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # a side of at most 64 (or 129 to 192): 128-wide tiles would be mostly
     # padding, so only the 64 x 64 choices; a side of 96 or 128 keeps them
     ((64, 32768, 4096), "dma_64x64x16_ksplit8_pipe "), ((32768, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
-    ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x64 "),
+    ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x16_ksplit8_pipe "),
     ((64, 65536, 1024), "dma_64x128x32 "), ((65536, 64, 1024), "dma_128x64x32 "),
     ((96, 32768, 4096), "dma_128x128x64_pipe_lw2 "), ((128, 32768, 4096), "dma_128x128x64_pipe_lw2 "),
     # a second round exactly half full (384 tiles): stream-K over the K split
