@@ -1524,9 +1524,11 @@ using Tile32x64K16S8 = MfmaTile<32, 64, 16, 1, 1, 8, 2>;   // 8 groups of 32 x 6
 using Tile64x32K16S8 = MfmaTile<64, 32, 16, 1, 1, 8, 2>;
 
 // Every configuration is one the shape rule (select_config) picks for some
-// shapes, or the register-staged fallback for rows too long for 32-bit
-// panel offsets; each also runs under gemm_f32_with_config for tests and
-// sweeps.
+// shapes, the register-staged fallback for rows too long for 32-bit panel
+// offsets, or one of the two plain 64 x 64 stream-K twins, which the rule no
+// longer picks (over K <= 512 a second round of tiles beats stream-K) but
+// which remain the simplest stream-K kernels (no K-split fold); each also
+// runs under gemm_f32_with_config for tests and sweeps.
 enum ConfigId {
     kCfgValu64 = 0,
     kCfgStaged128x128,
@@ -1825,12 +1827,16 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // x 8192: 45 against 126; 500^3: 9.8 against 16.3); with K <= 256, 4
     // groups (300 x 400 x 100: 6.7 against 7.2 for 8).  While 32 x 64 (64 x
     // 32) tiles fit in one round, 8 groups of those (640 x 640 x 2048: 25.9
-    // us against 39.3; 1024 x 512 x 1024: 17.2 against 24.7).
+    // us against 39.3; 1024 x 512 x 1024: 17.2 against 24.7), 32 x 64 ones
+    // first (their panels' wider B rows: 848 x 383 x 723 13.6 us against 14.2
+    // for 64 x 32; 700 x 600 x 1000: 15.8 against 16.2).
     const int64_t t32x32 = ceil_div(M, 32) * ceil_div(N, 32);
     if (t32x32 <= CU)
         return K > 256 ? kCfgDma32x32K32S8 : kCfgDma32x32K32S4;
-    if (N >= M ? tiles(kCfgDma32x64K16S8) <= CU : tiles(kCfgDma64x32K16S8) <= CU)
-        return N >= M ? kCfgDma32x64K16S8 : kCfgDma64x32K16S8;
+    if (tiles(kCfgDma32x64K16S8) <= CU)
+        return kCfgDma32x64K16S8;
+    if (tiles(kCfgDma64x32K16S8) <= CU)
+        return kCfgDma64x32K16S8;
     // The busiest CU has ceil(tiles / CUs) tiles.  The last round of tiles
     // leaves more than a fifth of the CU-rounds idle when this is true:
     auto unbalanced = [&](int c) {
@@ -1978,19 +1984,19 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 64 x 64 tiles.  Up to two per CU, the one or two 4-wave workgroups
     // leave each SIMD one or two waves, and 64-deep panels halve the
     // per-panel barrier stalls that then show, unless their last panel is
-    // at most half used (K % 64 in 1..32), which 32-deep panels avoid
-    // (600 x 3000 x 200: 14.2 us against 15.6; 956 x 1597 x 331: 18.9
-    // against 20.1; but 1280 x 1280 x 512: 23.7 against 24.1 for 32-deep
-    // panels, 1000 x 1000 x 300: 12.6 against 12.8); with more, several
+    // at most half used (K % 64 in 1..32), which 32-deep panels avoid, or K
+    // is under 256 (600 x 3000 x 200: 14.2 us against 15.6; 956 x 1597 x
+    // 331: 18.9 against 20.1; 1590 x 744 x 100: 11.0 against 11.4; but 1280
+    // x 1280 x 512: 23.7 against 24.1 for 32-deep panels, 1000 x 1000 x 300:
+    // 12.6 against 12.8); with more, several
     // workgroups share a CU and the smaller 32-deep panels (more resident
-    // workgroups) win.
-    // Barely more than one tile per CU: stream-K, so the few extra tiles do
-    // not double the time.
+    // workgroups) win.  Stream-K does not pay here, even barely past one
+    // round: with K <= 512 its clearing launch and split tiles cost more
+    // than the second round (1025 x 1023 x 300: 22.1 us against 17.6;
+    // 1590 x 744 x 100: 17.1 against 11.0).
     const int64_t t64 = tiles(kCfgDma64x64K64);
-    if (t64 > CU && 4 * t64 <= 5 * CU)
-        return deep_ok ? kCfgDma64x64K64SK : kCfgDma64x64K32SK;
     if (t64 <= 2 * CU)
-        return deep_ok && 64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) ? kCfgDma64x64K64 : kCfgDma64x64K32;
+        return deep_ok && K >= 256 && 64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) ? kCfgDma64x64K64 : kCfgDma64x64K32;
     return kCfgDma64x64K32;
 }
 

@@ -180,7 +180,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4 ") and "strip_rows=1" in text, text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 500, FAKE, 500, FAKE, ldb, FAKE, 1023)
-    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_sk "), text
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32 "), text
     k64 = gb.config_names().index("dma_64x64x64")
     rc, _ = gb.gemm_f32_describe(k64, 1024, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
     assert rc == gb.GEMM_F32_ERR_CONFIG
@@ -214,7 +214,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((256, 256, 8192), "dma_32x32x32_ksplit8 "), ((17, 33, 65), "dma_32x32x32_ksplit4 "),
     ((300, 400, 100), "dma_32x32x32_ksplit4 "), ((64, 2048, 2048), "dma_32x32x32_ksplit8 "),
     ((640, 640, 2048), "dma_32x64x16_ksplit8 "), ((512, 1024, 1024), "dma_32x64x16_ksplit8 "),
-    ((1024, 512, 1024), "dma_64x32x16_ksplit8 "), ((700, 600, 1000), "dma_64x32x16_ksplit8 "),
+    ((1024, 512, 1024), "dma_32x64x16_ksplit8 "), ((700, 600, 1000), "dma_32x64x16_ksplit8 "),
+    ((960, 544, 1000), "dma_64x32x16_ksplit8 "),
     # 272 tiles, 16 of them for a last row of 1-4 rows (rows x K <= 4096): one
     # round of K-split tiles and a strip of FMAs
     ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((1028, 1000, 1000), "dma_64x64x32_ksplit4 "),
@@ -226,7 +227,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1025, 1023, 3000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
     ((1100, 1100, 1100), "dma_64x64x32_ksplit4_sk "),
     ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "), ((1280, 1280, 1280), "dma_64x64x16_ksplit8_pipe "),
-    ((1025, 1023, 300), "dma_64x64x64_sk "),
+    ((1025, 1023, 300), "dma_64x64x64 "), ((1590, 744, 100), "dma_64x64x32 "),
     # two balanced rounds: the pipelined K split for K >= 1024, else 64 x 64
     ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe "), ((2048, 1024, 1024), "dma_64x64x16_ksplit8_pipe "),
     ((1400, 1400, 1000), "dma_64x64x64 "), ((2048, 1024, 768), "dma_64x64x64 "),
