@@ -60,18 +60,22 @@ struct GemmArgs {
     int slices;          // K slices of a split-K launch (1 otherwise)
     int64_t slab;        // floats between two slices' partial products in C
     int strip_rows;      // rows M - strip_rows .. M-1 lie below the tile grid
-                         // (tiles_m * BM = M - strip_rows): the last tile
-                         // row's workgroups compute them with FMAs
+                         // (tiles_m * BM = M - strip_rows): every workgroup
+                         // computes a share of their columns with FMAs
     int strip_cols;      // likewise columns N - strip_cols .. N-1, right of
-                         // the grid, for the last tile column (not together
-                         // with strip_rows)
+                         // the grid, every workgroup a share of their rows
+                         // (not together with strip_rows)
     int xcds;            // dies the device hands workgroups to round-robin
 };
 
-// Most rows a remainder strip may hold, and its largest K: the strip's rows
-// of A are staged in LDS next to the partial sums.
+// Most rows (columns) a remainder strip may hold, its largest K, and the
+// most columns (rows) of it one workgroup sums.
 constexpr int kMaxStripRows = 4;
 constexpr int kMaxStripK = 2048;
+constexpr int kMaxStripSpread = 8;
+constexpr int kMaxThreads = 1024;      // threads of the largest workgroup
+// LDS floats a strip block's partial sums take (strip_block), at most.
+constexpr int kStripRed = kMaxStripSpread * kMaxStripSpread * (kMaxThreads / 4 + 1);
 
 // ---------------------------------------------------------------------------
 // Tile scheduling
@@ -210,22 +214,18 @@ struct MfmaTile {
     static_assert(!kLoaderWave || (PIPE_ != 0 && KSPLIT_ == 1), "loader waves serve one pipelined group");
 };
 
-// The tile that also computes remainder strips (64 x 64, 32-deep panels, 4
-// K-split groups of 4 waves): the only one the shape rule pairs with a
-// strip.  The strip code lives in a separate instantiation of its kernel
-// (STRIP), so the plain one keeps its registers (60 VGPRs against 83).
-using StripTile = MfmaTile<64, 64, 32, 2, 2, 4>;
+// The tile that also computes remainder strips (64 x 64, 8 software-
+// pipelined one-wave K-split groups on 16-deep panels): the only one the
+// shape rule pairs with a strip.  The strip code lives in a separate
+// instantiation of its kernel (STRIP), so the plain one keeps its registers.
+using StripTile = MfmaTile<64, 64, 16, 1, 1, 8, 2, 8, 0, 1>;
 
-// Whether a direct-to-LDS tile's panel buffers hold a strip's partial sums
-// and A rows.
+// Whether a tile's panel buffers hold a strip block's partial sums.
 template <class T>
 constexpr bool strip_fits()
 {
     constexpr int stage = T::BM * T::BK + T::BK * T::BN;
-    constexpr int red_rows = T::kThreads / T::BN * kMaxStripRows * T::BN;
-    constexpr int red_cols = T::BM * kMaxStripRows * kWaveSize;
-    constexpr int red = red_rows > red_cols ? red_rows : red_cols;
-    return T::kThreads % T::BN == 0 && red + kMaxStripRows * kMaxStripK <= T::kSplit * T::kStages * stage;
+    return T::kThreads <= kMaxThreads && kStripRed <= T::kSplit * T::kStages * stage;
 }
 static_assert(strip_fits<StripTile>(), "strip space in the strip tile's panel buffers");
 
@@ -424,6 +424,99 @@ __device__ inline void poison_region(float *base, int floats, int t, int threads
 {
     for (int e = 4 * t; e < floats; e += 4 * threads)
         poison16(base + e);
+}
+
+// One workgroup's block of a remainder strip: C[ar0 + r][bc0 + c] =
+// sum over k of A[ar0 + r][k] * B[k][bc0 + c] for r < nr, c < nc (nr, nc <=
+// kMaxStripSpread), with vector FMAs.  Lane groups of CW threads share a k
+// and take one column each (c = tid % CW, nc <= CW), so a wave's B loads
+// cover 64 / CW rows of CW consecutive columns and its A loads 64 / CW
+// consecutive k of a row.  Thread tid takes k = tid / CW, + NT / CW, ...,
+// loads kBatch of them at a time (one memory latency per batch) and sums
+// them in k order; the NT / CW sums of each output are then added through
+// LDS (`red`, kStripRed floats) in thread order, 16 runs of consecutive
+// threads' sums and then the runs, so the result does not depend on
+// scheduling.  All NT threads call it (it has barriers).  Kept
+// out of line so that the tile kernel around it keeps its registers.
+template <int NT, int CW>
+__device__ __noinline__ void strip_block(const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
+                                         int64_t ldc, int K, int ar0, int nr, int bc0, int nc, float *red, int tid)
+{
+    constexpr int R = kMaxStripSpread;
+    constexpr int KS = NT / CW;                // k's one pass covers
+    constexpr int PAD = KS + 1;                // sums per output, padded against bank conflicts
+    constexpr int kBatch = 8;                  // k's per thread loaded at once
+    static_assert(NT % CW == 0 && R * CW * PAD <= kStripRed, "strip sums fit");
+    // A and B are global memory: address them as such (global instead of
+    // flat loads).
+    using gfloat = const __attribute__((address_space(1))) float;
+    gfloat *ga = (gfloat *)A, *gb = (gfloat *)B;
+    const int c = tid % CW, kk = tid / CW;
+    const bool on = c < nc && nr > 0;
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        acc[r] = 0.f;
+    if (on) {
+        for (int k0 = kk; k0 < K; k0 += kBatch * KS) {
+            float a[kBatch][R], b[kBatch];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int k = k0 + u * KS;
+                b[u] = k < K ? gb[(int64_t)k * ldb + bc0 + c] : 0.f;
+#pragma unroll
+                for (int r = 0; r < R; ++r)
+                    a[u][r] = k < K && r < nr ? ga[(int64_t)(ar0 + r) * lda + k] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+                if (k0 + u * KS < K) {
+#pragma unroll
+                    for (int r = 0; r < R; ++r)
+                        acc[r] = fmaf(a[u][r], b[u], acc[r]);
+                }
+        }
+    }
+    __syncthreads();
+    if constexpr (kPoisonLds) {
+        poison_region(red, R * CW * PAD / 4 * 4, tid, NT);
+        __syncthreads();
+    }
+    // `red` is LDS: address it as such (ds_* instead of flat accesses).
+    using lds_float = __attribute__((address_space(3))) float;
+    lds_float *sums = (lds_float *)red;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (on && r < nr)
+            sums[(r * CW + c) * PAD + kk] = acc[r];
+    __syncthreads();
+    // Each output's KS sums in kChunks runs of consecutive threads' sums,
+    // then the runs' totals, both in thread order.
+    // (A block has at most kMaxStripRows x kMaxStripSpread outputs.)
+    constexpr int kChunks = 16, kRun = KS / kChunks;
+    static_assert(KS % kChunks == 0 && NT >= kMaxStripRows * kMaxStripSpread * kChunks, "chunked sums");
+    float part = 0.f;
+    const int o = tid / kChunks, j = tid % kChunks;               // output o = r * nc + cc
+    if (o < nr * nc) {
+        const lds_float *v = sums + ((o / nc) * CW + o % nc) * PAD + j * kRun;
+        part = v[0];
+#pragma unroll
+        for (int i = 1; i < kRun; ++i)
+            part += v[i];
+    }
+    __syncthreads();
+    if (o < nr * nc)
+        sums[o * kChunks + j] = part;
+    __syncthreads();
+    if (tid < nr * nc) {
+        const lds_float *v = sums + tid * kChunks;
+        float sum = v[0];
+#pragma unroll
+        for (int i = 1; i < kChunks; ++i)
+            sum += v[i];
+        store_c(&C[(int64_t)(ar0 + tid / nc) * ldc + bc0 + tid % nc], sum);
+    }
+    __syncthreads();
 }
 
 // Chunk permutation of A-panel row r (BK/4 chunks of 16 bytes per row).
@@ -1190,150 +1283,35 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
             }
         }
 
-        // Remainder strip (data-parallel launches only): the workgroups of
-        // the last tile row also compute rows M-strip_rows .. M-1 of their
-        // columns with vector FMAs.  The strip's rows of A are first copied
-        // to LDS (read there as broadcasts).  The lanes of a wave take
-        // consecutive columns and the waves contiguous K slices; each lane
-        // sums its slice in k order, loading B 8 rows at a time, then the
-        // slices' sums are added in slice order through LDS, so the result
-        // does not depend on scheduling.
+        // Remainder strips (data-parallel launches only): rows M-R .. M-1
+        // below the tile grid (or columns N-R .. N-1 right of it) are summed
+        // with vector FMAs by every workgroup: the one running tile t takes
+        // w = ceil(N / tiles) of the strip's columns from t * w (of its rows,
+        // ceil(M / tiles) of them), at most kMaxStripSpread, so that no
+        // workgroup streams much of B (A); strip_block sums the block.
         if constexpr (STRIP)
-        if (g.strip_rows > 0 && tm == g.tiles_m - 1) {
-            constexpr int kSlices = T::kThreads / BN;
-            constexpr int kRed = kSlices * kMaxStripRows * BN;          // floats of partial sums
-            const int j = tid % BN, sl = tid / BN;
-            const int col = n0 + j;
-            const int r0 = g.M - g.strip_rows;
-            const int per = (g.K + kSlices - 1) / kSlices;
-            const int kb = sl * per, ke = min(g.K, kb + per);
+        if (g.strip_rows > 0 || g.strip_cols > 0) {
+            const int total = g.tiles_m * g.tiles_n;
+            int ar0, nr, bc0, nc;              // rows ar0 .. of A and C, columns bc0 .. of B and C
+            if (g.strip_rows > 0) {
+                const int w = (g.N + total - 1) / total;
+                ar0 = g.M - g.strip_rows;
+                nr = g.strip_rows;
+                bc0 = t * w;
+                nc = max(0, min(w, g.N - bc0));
+            } else {
+                const int h = (g.M + total - 1) / total;
+                ar0 = t * h;
+                nr = max(0, min(h, g.M - ar0));
+                bc0 = g.N - g.strip_cols;
+                nc = g.strip_cols;
+            }
             float *red = &lds[0][0][0];
-            float *sa = red + kRed;                  // strip_rows x K floats of A
             __syncthreads();
-            if constexpr (kPoisonLds) {
-                poison_region(red, (kRed + g.strip_rows * g.K + 3) / 4 * 4, tid, T::kThreads);
-                __syncthreads();
-            }
-            for (int e = tid; e < g.strip_rows * g.K; e += T::kThreads)
-                sa[e] = g.A[(int64_t)(r0 + e / g.K) * g.lda + e % g.K];
-            __syncthreads();
-            float part[kMaxStripRows] = {};
-            auto strip_sum = [&](auto rows) {
-                constexpr int R = decltype(rows)::value;
-                int k = kb;
-                for (; k + 8 <= ke; k += 8) {
-                    float bv[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-                        bv[u] = g.B[(int64_t)(k + u) * g.ldb + col];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u)
-#pragma unroll
-                        for (int r = 0; r < R; ++r)
-                            part[r] = fmaf(sa[r * g.K + k + u], bv[u], part[r]);
-                }
-                for (; k < ke; ++k) {
-                    const float bv = g.B[(int64_t)k * g.ldb + col];
-#pragma unroll
-                    for (int r = 0; r < R; ++r)
-                        part[r] = fmaf(sa[r * g.K + k], bv, part[r]);
-                }
-            };
-            if (col < g.N) {
-                switch (g.strip_rows) {
-                case 1: strip_sum(std::integral_constant<int, 1>()); break;
-                case 2: strip_sum(std::integral_constant<int, 2>()); break;
-                case 3: strip_sum(std::integral_constant<int, 3>()); break;
-                default: strip_sum(std::integral_constant<int, 4>()); break;
-                }
-            }
-#pragma unroll
-            for (int r = 0; r < kMaxStripRows; ++r)
-                red[(sl * kMaxStripRows + r) * BN + j] = part[r];
-            __syncthreads();
-            if (sl == 0 && col < g.N) {
-                for (int r = 0; r < g.strip_rows; ++r) {
-                    float sum = red[r * BN + j];
-                    for (int s2 = 1; s2 < kSlices; ++s2)
-                        sum += red[(s2 * kMaxStripRows + r) * BN + j];
-                    store_c(&cbase[(int64_t)(r0 + r) * g.ldc + col], sum);
-                }
-            }
-            __syncthreads();
-        }
-
-        // The same for columns right of the grid: the workgroups of the last
-        // tile column compute columns N-strip_cols .. N-1 of their rows.  The
-        // strip's columns of B are copied to LDS as rows ([c][k]).  Each wave
-        // takes BM / waves consecutive rows; the lanes of a wave split K
-        // (lane l takes k = l, l+64, ...), so A is read along its rows.  Each
-        // lane sums its k's in order, then one thread per output adds the 64
-        // lanes' sums in lane order through LDS.
-        if constexpr (STRIP)
-        if (g.strip_cols > 0 && tn == g.tiles_n - 1) {
-            constexpr int kWaves = T::kThreads / kWaveSize;
-            constexpr int kRowsPerWave = BM / kWaves;
-            constexpr int kRed = BM * kMaxStripRows * kWaveSize;        // floats of partial sums
-            static_assert(BM % kWaves == 0 && kRowsPerWave >= 1, "column strip rows");
-            const int w = tid / kWaveSize;
-            const int c0 = g.N - g.strip_cols;
-            float *red = &lds[0][0][0];
-            float *sb = red + kRed;                  // strip_cols x K floats of B, as [c][k]
-            __syncthreads();
-            if constexpr (kPoisonLds) {
-                poison_region(red, (kRed + g.strip_cols * g.K + 3) / 4 * 4, tid, T::kThreads);
-                __syncthreads();
-            }
-            for (int e = tid; e < g.strip_cols * g.K; e += T::kThreads)
-                sb[e] = g.B[(int64_t)(e % g.K) * g.ldb + c0 + e / g.K];
-            __syncthreads();
-            float part[kRowsPerWave][kMaxStripRows] = {};
-            // Rows past M-1 (in the last tile row) read row M-1 instead;
-            // their sums are never stored.
-            const float *arow[kRowsPerWave];
-#pragma unroll
-            for (int rr = 0; rr < kRowsPerWave; ++rr)
-                arow[rr] = g.A + (int64_t)min(m0 + w * kRowsPerWave + rr, g.M - 1) * g.lda;
-            auto strip_sum = [&](auto cols) {
-                constexpr int CC = decltype(cols)::value;
-#pragma unroll 4
-                for (int k = lane; k < g.K; k += kWaveSize) {
-                    float a[kRowsPerWave];
-#pragma unroll
-                    for (int rr = 0; rr < kRowsPerWave; ++rr)
-                        a[rr] = arow[rr][k];
-#pragma unroll
-                    for (int c = 0; c < CC; ++c) {
-                        const float b = sb[c * g.K + k];
-#pragma unroll
-                        for (int rr = 0; rr < kRowsPerWave; ++rr)
-                            part[rr][c] = fmaf(a[rr], b, part[rr][c]);
-                    }
-                }
-            };
-            switch (g.strip_cols) {
-            case 1: strip_sum(std::integral_constant<int, 1>()); break;
-            case 2: strip_sum(std::integral_constant<int, 2>()); break;
-            case 3: strip_sum(std::integral_constant<int, 3>()); break;
-            default: strip_sum(std::integral_constant<int, 4>()); break;
-            }
-#pragma unroll
-            for (int rr = 0; rr < kRowsPerWave; ++rr)
-#pragma unroll
-                for (int c = 0; c < kMaxStripRows; ++c)
-                    red[((w * kRowsPerWave + rr) * kMaxStripRows + c) * kWaveSize + lane] = part[rr][c];
-            __syncthreads();
-            for (int e = tid; e < BM * kMaxStripRows; e += T::kThreads) {
-                const int row = e / kMaxStripRows, c = e % kMaxStripRows;
-                if (c < g.strip_cols && m0 + row < g.M) {
-                    const float *v = &red[e * kWaveSize];
-                    float sum = v[0];
-                    for (int l = 1; l < kWaveSize; ++l)
-                        sum += v[l];
-                    store_c(&cbase[(int64_t)(m0 + row) * g.ldc + c0 + c], sum);
-                }
-            }
-            __syncthreads();
+            if (nc <= 4)
+                strip_block<T::kThreads, 4>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K, ar0, nr, bc0, nc, red, tid);
+            else
+                strip_block<T::kThreads, 8>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K, ar0, nr, bc0, nc, red, tid);
         }
     };
 
@@ -1930,26 +1908,26 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 2048: the 8 pipelined groups.
     const int64_t t32 = tiles(kCfgDma64x64K32);
     // A last tile row of at most kMaxStripRows rows that alone takes the
-    // tiles past one round: those rows become a strip computed with FMAs by
-    // the last full tile row, and the rest runs as one round of 4-group
-    // K-split tiles.  The strip's cost grows with rows x K (each of a
-    // workgroup's 16 waves reads K/16 rows of 64 B columns and does rows
-    // FMAs per k), so only up to 4096 (1025 x 1023 x 1000: 29.6 us against
-    // 37.3 for stream-K; 1026 x 1001 x 1001: 31.8 against 37.5; at 4 x 1500
-    // both take 44.8, at 3 x 2048 the strip is 10 % slower).
+    // tiles past one round: those rows become a strip computed with FMAs,
+    // spread over all workgroups, and the rest runs as one round of the 8
+    // pipelined K-split groups.  Strips stay up to rows x K = 4096, and each
+    // workgroup's share of the strip's columns up to kMaxStripSpread
+    // (1025 x 1023 x 1000: 26.8 us against 29.7 for the strip summed by the
+    // last tile row of 4-group K-split tiles, 37.3 for stream-K; 1000 x 1028
+    // x 1000: 26.7 against 35.0).
     const int64_t t_full = (M / 64) * ceil_div(N, 64);
-    static_assert(std::is_same<Tile64x64K32S4, StripTile>::value, "the strip tile is the 4-group K-split tile");
+    static_assert(std::is_same<Tile64x64K16S8P, StripTile>::value, "the strip tile is the 8-group pipelined K split");
     if (K > 512 && K < kMaxStripK && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
-        t_full <= CU && t32 > CU) {
+        t_full <= CU && t32 > CU && ceil_div(N, t_full) <= kMaxStripSpread) {
         strip_rows = M % 64;
-        return kCfgDma64x64K32S4;
+        return kCfgDma64x64K16S8P;
     }
     // The same for a last tile column of at most kMaxStripRows columns.
     const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
     if (K > 512 && K < kMaxStripK && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
-        t_full_n <= CU && t32 > CU) {
+        t_full_n <= CU && t32 > CU && ceil_div(M, t_full_n) <= kMaxStripSpread) {
         strip_cols = N % 64;
-        return kCfgDma64x64K32S4;
+        return kCfgDma64x64K16S8P;
     }
     if (K > 512 && t32 <= CU) {
         const int64_t k8 = 128 * ceil_div(ceil_div(K, 16), 8);   // K the busiest of the 8 groups covers
@@ -2060,14 +2038,17 @@ int make_plan(int config, int M, int N, int K, const float *A, int lda,
     } else if (kConfigs[c].dma && !dma_offsets_fit(kConfigs[c], lda, ldb)) {
         return GEMM_F32_ERR_CONFIG;   // this kernel cannot address such wide rows
     }
-    // The strip kernel sums at most kMaxStripRows rows (columns); the rule
-    // never plans a wider strip.
+    // The strip kernel sums at most kMaxStripRows rows (columns), and each
+    // workgroup at most kMaxStripSpread columns (rows) of them; the rule
+    // never plans more.
     if (strip > kMaxStripRows || strip_c > kMaxStripRows)
         return GEMM_F32_ERR_CONFIG;
     const int64_t tm = strip ? (M - strip) / kConfigs[c].bm : ceil_div(M, kConfigs[c].bm);
     const int64_t tn = strip_c ? (N - strip_c) / kConfigs[c].bn : ceil_div(N, kConfigs[c].bn);
     if (tm * tn > INT32_MAX)
         return GEMM_F32_ERR_DIM;
+    if ((strip && ceil_div(N, tm * tn) > kMaxStripSpread) || (strip_c && ceil_div(M, tm * tn) > kMaxStripSpread))
+        return GEMM_F32_ERR_CONFIG;
     plan->config = c;
     plan->strip_rows = strip;
     plan->strip_cols = strip_c;

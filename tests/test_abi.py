@@ -178,7 +178,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 1100, 1100, 1300, FAKE, 1300, FAKE, ldb, FAKE, 1100)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4_sk "), text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
-    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4 ") and "strip_rows=1" in text, text
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x16_ksplit8_pipe ") and "strip_rows=1" in text, text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 500, FAKE, 500, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32 "), text
     k64 = gb.config_names().index("dma_64x64x64")
@@ -218,9 +218,9 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((960, 544, 1000), "dma_64x32x16_ksplit8 "),
     # 272 tiles, 16 of them for a last row of 1-4 rows (rows x K <= 4096): one
     # round of K-split tiles and a strip of FMAs
-    ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((1028, 1000, 1000), "dma_64x64x32_ksplit4 "),
+    ((1025, 1023, 1000), "dma_64x64x16_ksplit8_pipe "), ((1028, 1000, 1000), "dma_64x64x16_ksplit8_pipe "),
     ((1025, 1023, 2048), "dma_64x64x32_ksplit4_sk "), ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "),
-    ((1023, 1025, 1000), "dma_64x64x32_ksplit4 "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
+    ((1023, 1025, 1000), "dma_64x64x16_ksplit8_pipe "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
     # 272, 289, 324 and 576 64 x 64 tiles: the last round would be under
     # half full; stream-K over the K-split tile.  400 tiles: two rounds of
     # the pipelined K split

@@ -372,7 +372,7 @@ def test_graph_capture_replays_match_eager(dev):
 
 
 GRAPH_PLANS = [((2048, 2048, 512), "dma_128x128x64_pipe_lw2 "), ((4096, 4096, 128), "dma_128x128x16_pipe "),
-               ((1025, 1023, 1000), "dma_64x64x32_ksplit4 "), ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
+               ((1025, 1023, 1000), "dma_64x64x16_ksplit8_pipe "), ((16384, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
                ((512, 512, 512), "dma_32x32x32_ksplit8 "), ((640, 640, 2048), "dma_32x64x16_ksplit8 "),
                ((1000, 1000, 600), "dma_64x64x32_pipe_lw2_s4 "), ((2560, 2560, 2560), "dma_128x128x64_pipe_lw2_sk ")]
 
