@@ -564,7 +564,10 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
 STRIP = [((1025, 1023, 1000), "strip_rows=1"), ((1028, 1000, 1000), "strip_rows=4"),
          ((1026, 1001, 1001), "strip_rows=2"), ((1027, 1024, 1300), "strip_rows=3"),
          ((1023, 1025, 1000), "strip_cols=1"), ((1000, 1028, 1000), "strip_cols=4"),
-         ((1001, 1026, 1001), "strip_cols=2"), ((1024, 1027, 1300), "strip_cols=3")]
+         ((1001, 1026, 1001), "strip_cols=2"), ((1024, 1027, 1300), "strip_cols=3"),
+         # the strip's shortest and longest K
+         ((1025, 1023, 513), "strip_rows=1"), ((1025, 1023, 2047), "strip_rows=1"),
+         ((1023, 1025, 2047), "strip_cols=1")]
 
 
 @pytest.mark.parametrize("shape,strip", STRIP, ids=["x".join(map(str, s)) for s, _ in STRIP])
@@ -594,6 +597,27 @@ def test_wide_remainders_bit_exact_and_padding_kept(dev, shape):
     assert_bit_exact(got, oracle.gemm(A, B), f"{shape}")
     body = full[:M * (N + 3)].reshape(M, N + 3)
     assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 3):]).all()
+
+
+@pytest.mark.parametrize("shape", [(1025, 1023, 1000), (1023, 1025, 1000)], ids=["rows", "cols"])
+def test_strips_special_values_classified_as_the_oracle(dev, shape):
+    """NaN and +-Inf in the strip's rows (columns) of A (B) and elsewhere:
+    every element of C, strip included, is NaN, +Inf, -Inf or finite exactly
+    when the oracle's is (the classification does not depend on summation
+    order), and finite elements are within tolerance."""
+    M, N, K = shape
+    A, B = special_operands(M, N, K)
+    A[M - 1, 7] = np.inf          # the strip row (or, for columns, a row the strip spans)
+    B[11, N - 1] = -np.inf        # the strip column (or a column the row strip spans)
+    got, _ = gpu_gemm(A, B, -1, dev)
+    with np.errstate(invalid="ignore"):
+        ref = oracle.gemm(A, B)
+    for name, f in {"nan": np.isnan, "+inf": np.isposinf, "-inf": np.isneginf}.items():
+        bad = np.flatnonzero(f(got) != f(ref))
+        assert bad.size == 0, f"{shape}: {bad.size} elements differ in being {name}; first {bad[0]}"
+    fin = np.isfinite(ref)
+    assert np.isfinite(ref[M - 1]).sum() < N or np.isfinite(ref[:, N - 1]).sum() < M
+    assert_close(got[fin], ref[fin], f"strip special {shape} finite part")
 
 
 @pytest.mark.parametrize("shape", [(1026, 1001, 1001), (1001, 1026, 1001)], ids=["rows", "cols"])
