@@ -446,7 +446,7 @@ __device__ __noinline__ void strip_block(const float *A, int64_t lda, const floa
     constexpr int KS = NT / CW;                // k's one pass covers
     constexpr int PAD = KS + 1;                // sums per output, padded against bank conflicts
     constexpr int kBatch = 8;                  // k's per thread loaded at once
-    static_assert(NT % CW == 0 && R * CW * PAD <= kStripRed, "strip sums fit");
+    static_assert(NT % CW == 0 && (R * CW * PAD + 3) / 4 * 4 <= kStripRed, "strip sums fit");
     // A and B are global memory: address them as such (global instead of
     // flat loads).
     using gfloat = const __attribute__((address_space(1))) float;
@@ -479,7 +479,7 @@ __device__ __noinline__ void strip_block(const float *A, int64_t lda, const floa
     }
     __syncthreads();
     if constexpr (kPoisonLds) {
-        poison_region(red, R * CW * PAD / 4 * 4, tid, NT);
+        poison_region(red, (R * CW * PAD + 3) / 4 * 4, tid, NT);
         __syncthreads();
     }
     // `red` is LDS: address it as such (ds_* instead of flat accesses).
