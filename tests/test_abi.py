@@ -251,6 +251,10 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((96, 32768, 4096), "dma_128x128x64_pipe_lw2 "), ((128, 32768, 4096), "dma_128x128x64_pipe_lw2 "),
     # a second round exactly half full (384 tiles): stream-K over the K split
     ((64, 24576, 4096), "dma_64x64x32_ksplit4_sk "), ((128, 12288, 12000), "dma_64x64x32_ksplit4_sk "),
+    # unless 64-wide tiles pad a side under 192 by a third more than 32-wide
+    # ones: 32 x 64 (64 x 32) tiles of the 8-group K split
+    ((95, 8926, 1248), "dma_32x64x16_ksplit8 "), ((8926, 95, 1248), "dma_64x32x16_ksplit8 "),
+    ((80, 12000, 2000), "dma_32x64x16_ksplit8 "), ((96, 8192, 1024), "dma_64x64x16_ksplit8_pipe "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe_lw2 "),
 ])
