@@ -1942,20 +1942,22 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // (A last round exactly half full too: 384 tiles, 64 x 24576 x 4096:
     // 126 us against 139 for the 8 pipelined groups; 24576 x 64 x 8192: 249
     // against 267.)
-    // Unless a side under 192 is padded a third more by 64-wide tiles than
-    // by 32-wide ones: then 32 x 64 (64 x 32) tiles of the 8 one-wave
-    // K-split groups, in up to three rounds, do less work (95 x 8926 x 1248:
-    // 32.5 us against 41.4 for stream-K; 8926 x 95 x 1248: 33.3 against
-    // 42.0; 80 x 12000 x 2000: 65.9 against 69.6).
-    if (K > 512 && (K >= 1100 || t32 <= 5 * CU / 4) && t32 <= 3 * CU &&
-        2 * last <= CU) {
-        auto pads_third_more = [](int side) { return side < 192 && 3 * ceil_div(side, 64) * 64 >= 4 * ceil_div(side, 32) * 32; };
+    // Past one round, a side under 192 that 64-wide tiles pad a third more
+    // than 32-wide ones: 32 x 64 (64 x 32) tiles of the 8 one-wave K-split
+    // groups, in up to three rounds, do less work (95 x 8926 x 1248: 32.5 us
+    // against 41.4 for stream-K; 8926 x 95 x 1248: 33.3 against 42.0; 80 x
+    // 12000 x 2000: 65.9 against 69.6; 15133 x 90 x 3196: 101.4 against 106.8
+    // for 64 x 64 tiles of the 8 pipelined groups).
+    auto pads_third_more = [](int side) { return side < 192 && 3 * ceil_div(side, 64) * 64 >= 4 * ceil_div(side, 32) * 32; };
+    if (K > 512 && t32 <= 3 * CU) {
         if (pads_third_more(M) && tiles(kCfgDma32x64K16S8) <= 3 * CU)
             return kCfgDma32x64K16S8;
         if (pads_third_more(N) && tiles(kCfgDma64x32K16S8) <= 3 * CU)
             return kCfgDma64x32K16S8;
-        return kCfgDma64x64K32S4SK;
     }
+    if (K > 512 && (K >= 1100 || t32 <= 5 * CU / 4) && t32 <= 3 * CU &&
+        2 * last <= CU)
+        return kCfgDma64x64K32S4SK;
     // Two rounds favour the 8 pipelined groups from K = 1024 on (2048 x
     // 1024 x 1024: 39.3 us against 42.1 for 64 x 64 tiles of 4 waves; 1600
     // x 1200 x 1200: 45.2 against 48.5; 2048 x 1024 x 1100: 45.5 against

@@ -255,6 +255,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # ones: 32 x 64 (64 x 32) tiles of the 8-group K split
     ((95, 8926, 1248), "dma_32x64x16_ksplit8 "), ((8926, 95, 1248), "dma_64x32x16_ksplit8 "),
     ((80, 12000, 2000), "dma_32x64x16_ksplit8 "), ((96, 8192, 1024), "dma_64x64x16_ksplit8_pipe "),
+    ((15133, 90, 3196), "dma_64x32x16_ksplit8 "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe_lw2 "),
 ])
