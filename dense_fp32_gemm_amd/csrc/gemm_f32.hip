@@ -68,10 +68,9 @@ struct GemmArgs {
     int xcds;            // dies the device hands workgroups to round-robin
 };
 
-// Most rows (columns) a remainder strip may hold, its largest K, and the
-// most columns (rows) of it one workgroup sums.
+// Most rows (columns) a remainder strip may hold, and the most columns
+// (rows) of it one workgroup sums.
 constexpr int kMaxStripRows = 4;
-constexpr int kMaxStripK = 2048;
 constexpr int kMaxStripSpread = 8;
 constexpr int kMaxThreads = 1024;      // threads of the largest workgroup
 // LDS floats a strip block's partial sums take (strip_block), at most.
@@ -1325,12 +1324,24 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
     } else if (SK) {
         int64_t lo, hi;
         streamk_range(xcd_contiguous(blockIdx.x, gridDim.x, g.xcds), gridDim.x, (int64_t)total * ktiles, lo, hi);
-        while (lo < hi) {
-            const int t = (int)(lo / ktiles);
-            const int p0 = (int)(lo - (int64_t)t * ktiles);
-            const int p1 = hi - lo < ktiles - p0 ? p0 + (int)(hi - lo) : ktiles;
-            work(t, p0, p1);
-            lo += p1 - p0;
+        // The range is the end of one tile (from panel lo % ktiles), whole
+        // tiles, and the start of another (panels 0 .. hi % ktiles).  Whole
+        // tiles go first and the start piece next, so that most workgroups
+        // are at the same K-panel at the same time and share the panels'
+        // rows of A and columns of B in L2; the end piece goes last.
+        const int first = (int)((lo + ktiles - 1) / ktiles);   // first tile starting at or after lo
+        const int last = (int)(hi / ktiles);                    // tile holding panel hi (or one past)
+        const int p_lo = (int)(lo % ktiles), p_hi = (int)(hi % ktiles);
+        if (lo >= hi) {
+        } else if (first > last) {
+            work(last, p_lo, p_hi);                             // inside one tile
+        } else {
+            for (int t = first; t < last; ++t)
+                work(t, 0, ktiles);
+            if (p_hi > 0)
+                work(last, 0, p_hi);
+            if (p_lo > 0)
+                work(first - 1, p_lo, ktiles);
         }
     } else {
         for (int w = blockIdx.x; w < total; w += gridDim.x)
@@ -1533,6 +1544,7 @@ enum ConfigId {
     kCfgDma64x32K16S8,
     kCfgDma128x128K32P,
     kCfgDma64x64K32PL2S4,
+    kCfgDma64x64K16S8PSK,
     kNumConfigs
 };
 
@@ -1682,6 +1694,7 @@ const ConfigInfo kConfigs[kNumConfigs] = {
     config_dma<Tile64x32K16S8>("dma_64x32x16_ksplit8"),
     config_dma<Tile128x128K32P, true>("dma_128x128x32_pipe"),
     config_dma<Tile64x64K32PL2S4>("dma_64x64x32_pipe_lw2_s4"),
+    config_streamk<Tile64x64K16S8P>("dma_64x64x16_ksplit8_pipe_sk"),
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1768,13 +1781,13 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    32-deep panels (1000 x 1000 x 600: 17.6 us against 18.1); a last tile row
 //    (column) of 1-4 rows (columns) past one round: one round of the 4-group
 //    K-split tile, the remainder computed as a strip;
-//  * up to three rounds of 64 x 64 tiles with a last round at most half full:
-//    stream-K over the 4-group K-split tile, past 320 tiles only with K >=
-//    1100 (1200 x 1200 x 4096: 120 us against 149 for 64 x 64; 1536^3: 81
-//    against 83; (1025, 1023, 1000): 37.2 against 42.3); otherwise two
-//    rounds with K >= 1024, or three with K >= 2048: the 8 pipelined groups
-//    (1300 x 1300 x 4096: 136 us against 149; 2048 x 1536 x 2048: 101
-//    against 110);
+//  * up to three rounds of 64 x 64 tiles, K >= 950 and idle CU-rounds x K
+//    large enough: stream-K over the 8 pipelined groups (1536^3: 70 us
+//    against 82 for stream-K over 4 groups; 1025 x 1025 x 4096: 87 against
+//    104), over the 4-group K split instead just past one round with K <
+//    1536; otherwise two rounds with K >= 1024, or three with K >= 2048:
+//    whole tiles of the 8 pipelined groups (1300 x 1300 x 4096: 136 us
+//    against 149; 2048 x 1536 x 2048: 101 against 110);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
 //    else 64 x 64.
 // Below the largest tile the choices use 32- or 64-deep K-panels: those
@@ -1903,9 +1916,10 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // groups against 27.1; 1000^3: 23.7 against 24.0, 25.1 for 4 K-split
     // groups of 4 waves; 1024 x 1024 x 640: 16.0 against 17.2; but 800 x
     // 1200 x 650, 41 panels over 8 groups: 18.8 against 18.3, and 1000 x
-    // 1000 x 600: 18.1 against 17.6); a last round at most half full:
-    // stream-K over the 4-group K-split tile; two rounds otherwise, with K >=
-    // 2048: the 8 pipelined groups.
+    // 1000 x 600: 18.1 against 17.6).  Past one round: stream-K over the 8
+    // pipelined groups where enough of the rounds would idle, over the
+    // 4-group K split just past one round; else whole tiles of the 8 groups
+    // for two rounds with K >= 1024 or three with K >= 2048.
     const int64_t t32 = tiles(kCfgDma64x64K32);
     // A last tile row of at most kMaxStripRows rows that alone takes the
     // tiles past one round: those rows become a strip computed with FMAs,
@@ -1914,17 +1928,18 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // workgroup's share of the strip's columns up to kMaxStripSpread
     // (1025 x 1023 x 1000: 26.8 us against 29.7 for the strip summed by the
     // last tile row of 4-group K-split tiles, 37.3 for stream-K; 1000 x 1028
-    // x 1000: 26.7 against 35.0).
+    // x 1000: 26.7 against 35.0; 1025 x 1023 x 3000: 58.2 against 65.2 for
+    // stream-K over the 8 pipelined groups).
     const int64_t t_full = (M / 64) * ceil_div(N, 64);
     static_assert(std::is_same<Tile64x64K16S8P, StripTile>::value, "the strip tile is the 8-group pipelined K split");
-    if (K > 512 && K < kMaxStripK && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
+    if (K > 512 && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
         t_full <= CU && t32 > CU && ceil_div(N, t_full) <= kMaxStripSpread) {
         strip_rows = M % 64;
         return kCfgDma64x64K16S8P;
     }
     // The same for a last tile column of at most kMaxStripRows columns.
     const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
-    if (K > 512 && K < kMaxStripK && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
+    if (K > 512 && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
         t_full_n <= CU && t32 > CU && ceil_div(M, t_full_n) <= kMaxStripSpread) {
         strip_cols = N % 64;
         return kCfgDma64x64K16S8P;
@@ -1934,14 +1949,6 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         const int64_t k4 = 32 * ceil_div(K, 32);                  // K the loader-wave tile covers
         return K >= 1536 || (K >= 640 && 8 * k8 <= 9 * k4) ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
     }
-    const int64_t last = t32 - (ceil_div(t32, CU) - 1) * CU;   // tiles in the last round
-    // (Past 320 tiles only with K >= 1100: below it the K-split groups'
-    // fold and stream-K's extra launch cost more than the idle CUs;
-    // 1600 x 1500 x 800: 53.7 us against 46.1 for 64 x 64 tiles; 1200 x 1200
-    // x 1000: 43.1 against 41.4; but 1100 x 1100 x 1100: 43.6 against 44.9.)
-    // (A last round exactly half full too: 384 tiles, 64 x 24576 x 4096:
-    // 126 us against 139 for the 8 pipelined groups; 24576 x 64 x 8192: 249
-    // against 267.)
     // Past one round, a side under 192 that 64-wide tiles pad a third more
     // than 32-wide ones: 32 x 64 (64 x 32) tiles of the 8 one-wave K-split
     // groups, in up to three rounds, do less work (95 x 8926 x 1248: 32.5 us
@@ -1955,8 +1962,20 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         if (pads_third_more(N) && tiles(kCfgDma64x32K16S8) <= 3 * CU)
             return kCfgDma64x32K16S8;
     }
-    if (K > 512 && (K >= 1100 || t32 <= 5 * CU / 4) && t32 <= 3 * CU &&
-        2 * last <= CU)
+    // Stream-K over the 8 pipelined groups where the idle share of the
+    // CU-rounds times K reaches 320 (from K = 950 on; 1025 x 1025 x 4096: 87
+    // us against 104 for the 4-group K split; 808 x 1496 x 6456: 135 against
+    // 166; 868 x 1930 x 5448, last round 70 % full: 157 against 170 for whole
+    // tiles of the 8 groups; 1249 x 1618 x 999: 55.0 against 57.7; but 1197 x
+    // 2414 x 2779, 94 % full: 142 against 141, and 3280 x 682 x 1149, 75 %:
+    // 66.6 against 64.4 for 64 x 64 tiles), except just past one round with
+    // K < 1536, where the 4-group K split's lighter pieces win (574 x 1850 x
+    // 1256: 40.6 us against 43.0).
+    const int64_t rounds = ceil_div(t32, CU);
+    if (K >= 950 && t32 <= 3 * CU && (rounds * CU - t32) * K >= 320 * rounds * CU &&
+        (t32 > 5 * CU / 4 || K >= 1536))
+        return kCfgDma64x64K16S8PSK;
+    if (K > 512 && t32 <= 5 * CU / 4)
         return kCfgDma64x64K32S4SK;
     // Two rounds favour the 8 pipelined groups from K = 1024 on (2048 x
     // 1024 x 1024: 39.3 us against 42.1 for 64 x 64 tiles of 4 waves; 1600

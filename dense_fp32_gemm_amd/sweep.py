@@ -11,7 +11,10 @@ configuration's C must equal, bit for bit, the C of a fixed reference kernel
 kernels), otherwise it is reported as failing and not timed.  (The parity
 tests tie the vector-FMA kernel itself to the CPU oracle.)  Configurations that pass are then timed
 on uniform[-1,1) operands (hipEvents around each call, after at least
---warmup calls and 0.2 s of warm-up) and ranked by mean time.  This is how the shape -> configuration table in
+--warmup calls and 0.2 s of warm-up) and ranked by mean time.  The plan the
+shape rule makes (config -1) is checked and timed as one more candidate,
+named auto:<configuration>, since it can differ from every forced
+configuration (a remainder strip).  This is how the shape -> configuration table in
 gemm_f32.hip is chosen; the Lecture 12 final-project page's sweep.cu follows
 the same "correct first, then fast" order for its block/tile/coarsening
 search.
@@ -57,20 +60,26 @@ def sweep_shape(torch, shape, configs, steps, warmup, log=print):
     torch.cuda.synchronize()
     if rc != gb.GEMM_F32_OK or not bool(torch.isfinite(ref).all()):
         raise RuntimeError(f"reference kernel failed on {shape}: {gb.gemm_f32_status_string(rc)}")
+    # The automatic plan (config -1) runs as a candidate of its own: it can
+    # differ from every forced configuration (a remainder strip).
+    _, plan = gb.gemm_f32_describe(-1, M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)
+    strip = [w for w in plan.split() if w.startswith("strip_")]
+    names = {c: gb.gemm_f32_config_name(c) for c in configs}
+    names[-1] = "auto:" + (plan.split() or ["?"])[0] + "".join(" " + w for w in strip)
     passed = []
-    for c in configs:
+    for c in list(configs) + [-1]:
         C.fill_(float("nan"))
         rc = _run(torch, c, A, B, C, stream)
         torch.cuda.synchronize()
         if rc != gb.GEMM_F32_OK:
-            rows.append(dict(M=M, N=N, K=K, config=gb.gemm_f32_config_name(c), ok=False,
+            rows.append(dict(M=M, N=N, K=K, config=names[c], ok=False, auto=c == -1,
                              note=gb.gemm_f32_status_string(rc)))
             continue
         ok = bool(torch.equal(C, ref))
         if ok:
             passed.append(c)
         else:
-            rows.append(dict(M=M, N=N, K=K, config=gb.gemm_f32_config_name(c), ok=False,
+            rows.append(dict(M=M, N=N, K=K, config=names[c], ok=False, auto=c == -1,
                              note="differs on quarter-step operands"))
     del A, B, qa, qb, ref
     ua, ub = inputs.uniform(M, N, K)
@@ -98,16 +107,13 @@ def sweep_shape(torch, shape, configs, steps, warmup, log=print):
             e1.record(stream)
         torch.cuda.synchronize()
         ms = np.array([e0.elapsed_time(e1) for e0, e1 in ev])
-        row = dict(M=M, N=N, K=K, config=gb.gemm_f32_config_name(c), ok=True, note="",
+        row = dict(M=M, N=N, K=K, config=names[c], ok=True, note="", auto=c == -1,
                    ms_mean=float(ms.mean()), ms_median=float(np.median(ms)), ms_min=float(ms.min()),
                    tflops=flop / (ms.mean() * 1e-3) / 1e12, gbs=nbytes / (ms.mean() * 1e-3) / 1e9)
         rows.append(row)
-    _, auto = gb.gemm_f32_describe(-1, M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)
-    auto = auto.split()[0]
     timed = sorted((r for r in rows if r["ok"]), key=lambda r: r["ms_mean"])
     for rank, r in enumerate(timed):
         r["rank"] = rank + 1
-        r["auto"] = r["config"] == auto
         log(f"{M:>6} {N:>6} {K:>6}  #{rank + 1:<2} {r['config']:<20} {r['ms_mean'] * 1e3:10.1f} us "
             f"{r['tflops']:8.2f} TFLOPS {r['gbs']:8.1f} GB/s{'  <- auto' if r['auto'] else ''}")
     for r in rows:

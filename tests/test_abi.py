@@ -176,7 +176,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     rc, text = gb.gemm_f32_describe(-1, 3072, 3072, 3072, FAKE, 3072, FAKE, ldb, FAKE, 3072)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_128x128x32_w16_sk "), text
     rc, text = gb.gemm_f32_describe(-1, 1100, 1100, 1300, FAKE, 1300, FAKE, ldb, FAKE, 1100)
-    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32_ksplit4_sk "), text
+    assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x16_ksplit8_pipe_sk "), text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x16_ksplit8_pipe ") and "strip_rows=1" in text, text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 500, FAKE, 500, FAKE, ldb, FAKE, 1023)
@@ -219,17 +219,20 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # 272 tiles, 16 of them for a last row of 1-4 rows (rows x K <= 4096): one
     # round of K-split tiles and a strip of FMAs
     ((1025, 1023, 1000), "dma_64x64x16_ksplit8_pipe "), ((1028, 1000, 1000), "dma_64x64x16_ksplit8_pipe "),
-    ((1025, 1023, 2048), "dma_64x64x32_ksplit4_sk "), ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "),
-    ((1023, 1025, 1000), "dma_64x64x16_ksplit8_pipe "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
-    # 272, 289, 324 and 576 64 x 64 tiles: the last round would be under
-    # half full; stream-K over the K-split tile.  400 tiles: two rounds of
-    # the pipelined K split
-    ((1025, 1023, 3000), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 4096), "dma_64x64x32_ksplit4_sk "),
-    ((1100, 1100, 1100), "dma_64x64x32_ksplit4_sk "),
-    ((1536, 1536, 1536), "dma_64x64x32_ksplit4_sk "), ((1280, 1280, 1280), "dma_64x64x16_ksplit8_pipe "),
+    ((1025, 1023, 2048), "dma_64x64x16_ksplit8_pipe "), ((1025, 1023, 3000), "dma_64x64x16_ksplit8_pipe "),
+    ((1023, 1025, 1000), "dma_64x64x16_ksplit8_pipe "),
+    # just past one round with K < 1536 (rows x K over 4096): stream-K over
+    # the 4-group K split
+    ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
+    # 289, 324, 441 and 576 64 x 64 tiles: the idle CU-rounds times K are
+    # large enough for stream-K over the 8 pipelined groups.  400 tiles (a
+    # last round 56 % full) with K = 1280: two rounds of the 8 groups
+    ((1025, 1025, 4096), "dma_64x64x16_ksplit8_pipe_sk "),
+    ((1100, 1100, 1100), "dma_64x64x16_ksplit8_pipe_sk "), ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe_sk "),
+    ((1536, 1536, 1536), "dma_64x64x16_ksplit8_pipe_sk "), ((1280, 1280, 1280), "dma_64x64x16_ksplit8_pipe "),
     ((1025, 1023, 300), "dma_64x64x64 "), ((1590, 744, 100), "dma_64x64x32 "),
     # two balanced rounds: the pipelined K split for K >= 1024, else 64 x 64
-    ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe "), ((2048, 1024, 1024), "dma_64x64x16_ksplit8_pipe "),
+    ((2048, 1024, 1024), "dma_64x64x16_ksplit8_pipe "),
     ((1400, 1400, 1000), "dma_64x64x64 "), ((2048, 1024, 768), "dma_64x64x64 "),
     # three rounds: the pipelined K split for K >= 2048; more rounds: 4-wave
     # 64 x 64 tiles, several per CU
@@ -249,8 +252,9 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x16_ksplit8_pipe "),
     ((64, 65536, 1024), "dma_64x128x32 "), ((65536, 64, 1024), "dma_128x64x32 "),
     ((96, 32768, 4096), "dma_128x128x64_pipe_lw2 "), ((128, 32768, 4096), "dma_128x128x64_pipe_lw2 "),
-    # a second round exactly half full (384 tiles): stream-K over the K split
-    ((64, 24576, 4096), "dma_64x64x32_ksplit4_sk "), ((128, 12288, 12000), "dma_64x64x32_ksplit4_sk "),
+    # a second round exactly half full (384 tiles): stream-K over the 8
+    # pipelined groups
+    ((64, 24576, 4096), "dma_64x64x16_ksplit8_pipe_sk "), ((128, 12288, 12000), "dma_64x64x16_ksplit8_pipe_sk "),
     # unless 64-wide tiles pad a side under 192 by a third more than 32-wide
     # ones: 32 x 64 (64 x 32) tiles of the 8-group K split
     ((95, 8926, 1248), "dma_32x64x16_ksplit8 "), ((8926, 95, 1248), "dma_64x32x16_ksplit8 "),

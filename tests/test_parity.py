@@ -515,17 +515,19 @@ def test_b_chunks_crossing_column_n_leave_c_clean(dev, config):
         assert np.isnan(body[:, N:]).all() and np.isnan(full[off[2] + M * ldc:]).all()
 
 
-def test_streamk_in_graph_and_on_concurrent_streams(dev):
+@pytest.mark.parametrize("shape,expect", [((1100, 1100, 1100), "dma_64x64x16_ksplit8_pipe_sk "),
+                                          ((574, 1850, 1256), "dma_64x64x32_ksplit4_sk ")])
+def test_streamk_in_graph_and_on_concurrent_streams(dev, shape, expect):
     """The stream-K plan is two kernels (clear the shared tiles, then the
     workers' atomic adds) and no memset: it captures into a HIP graph whose
     replays reproduce the eager result bit for bit, and two calls running at
     once on different streams share nothing."""
-    M, N, K = 1100, 1100, 1100
+    M, N, K = shape
     A, B = operands("uniform", M, N, K)
     dA = torch.from_numpy(A).to(dev)
     dB = torch.from_numpy(B).to(dev)
     rc, desc = gb.gemm_f32_describe(-1, M, N, K, dA.data_ptr(), K, dB.data_ptr(), N, dA.data_ptr(), N)
-    assert desc.startswith("dma_64x64x32_ksplit4_sk "), desc
+    assert desc.startswith(expect), desc
     say(f"stream-K eager, graph and concurrent streams, {M}x{N}x{K}")
     eager = gb.matmul(dA, dB)
     torch.cuda.synchronize()
@@ -558,16 +560,18 @@ def test_streamk_in_graph_and_on_concurrent_streams(dev):
 
 
 # ---------------------------------------------------------------------------
-# Remainder strips: 1-4 rows below one round of K-split tiles, computed with
-# FMAs by the last tile row's workgroups.
+# Remainder strips: 1-4 rows (columns) past one round of K-split tiles,
+# computed with FMAs, spread over all the tiles' workgroups.
 # ---------------------------------------------------------------------------
 STRIP = [((1025, 1023, 1000), "strip_rows=1"), ((1028, 1000, 1000), "strip_rows=4"),
          ((1026, 1001, 1001), "strip_rows=2"), ((1027, 1024, 1300), "strip_rows=3"),
          ((1023, 1025, 1000), "strip_cols=1"), ((1000, 1028, 1000), "strip_cols=4"),
          ((1001, 1026, 1001), "strip_cols=2"), ((1024, 1027, 1300), "strip_cols=3"),
-         # the strip's shortest and longest K
+         # the strip's shortest and longest K (rows x K up to 4096)
          ((1025, 1023, 513), "strip_rows=1"), ((1025, 1023, 2047), "strip_rows=1"),
-         ((1023, 1025, 2047), "strip_cols=1")]
+         ((1023, 1025, 2047), "strip_cols=1"), ((1025, 1023, 4096), "strip_rows=1"),
+         ((1023, 1025, 4096), "strip_cols=1"), ((1026, 1023, 2048), "strip_rows=2"),
+         ((1025, 1000, 2500), "strip_rows=1")]
 
 
 @pytest.mark.parametrize("shape,strip", STRIP, ids=["x".join(map(str, s)) for s, _ in STRIP])

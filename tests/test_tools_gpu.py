@@ -25,8 +25,20 @@ def test_sweep_checks_every_configuration(cuda):
     from dense_fp32_gemm_amd import sweep
     rows = sweep.sweep_shape(cuda, (300, 270, 77), list(range(gb.gemm_f32_num_configs())),
                              steps=2, warmup=1, log=lambda s: None)
-    assert len(rows) == gb.gemm_f32_num_configs()
+    assert len(rows) == gb.gemm_f32_num_configs() + 1
     assert all(r["ok"] for r in rows), [r for r in rows if not r["ok"]]
+    auto = [r for r in rows if r["auto"]]
+    assert len(auto) == 1 and auto[0]["config"] == "auto:dma_32x32x32_ksplit4", auto
+
+
+def test_sweep_times_the_strip_plan(cuda):
+    """A strip plan is not any forced configuration: the sweep times it as
+    its own candidate."""
+    from dense_fp32_gemm_amd import sweep
+    cfg = gb.config_names().index("dma_64x64x16_ksplit8_pipe")
+    rows = sweep.sweep_shape(cuda, (1025, 1023, 1000), [cfg], steps=2, warmup=1, log=lambda s: None)
+    assert [r["config"] for r in rows if r["auto"]] == ["auto:dma_64x64x16_ksplit8_pipe strip_rows=1"], rows
+    assert all(r["ok"] for r in rows), rows
 
 
 def test_report_row(cuda):
