@@ -1856,16 +1856,18 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     if (!thin && K <= 1024 && tiles(kCfgDma128x128K16P) >= 4 * CU)
         return kCfgDma128x128K16P;
     // 256 x 256 tiles: whole ones when they fill the rounds; stream-K over
-    // them only for K >= 3072 and when 128 x 128 tiles would not fill their
-    // rounds either (6400 x 6400 x 4096: 2317 us against 2373 for stream-K
-    // over 128 x 128 tiles; but 6478 x 5640 x 3472, 2295 of 2304 128 x 128
-    // slots used: 1796 against 1909); otherwise the 128 x 128 choices
-    // (7369 x 2892 x 2379: 794 against 829; 3813 x 6105 x 766: 281 against
-    // 354).
+    // them only for K >= 3072, at least two rounds of them, and when 128 x
+    // 128 tiles would not fill their rounds either (7168 x 6656 x 4096: 2649
+    // us against 2676 for stream-K over 128 x 128 tiles; but 5500 x 5500 x
+    // 3500, 1.9 rounds: 1561 against 1487; 4451 x 4749 x 4858, 1.3 rounds:
+    // 1521 against 1457; and 6478 x 5640 x 3472, 2295 of 2304 128 x 128
+    // slots used: 1796 against 1909 for 256 x 256 stream-K); otherwise the
+    // 128 x 128 choices (7369 x 2892 x 2379: 794 against 829; 3813 x 6105 x
+    // 766: 281 against 354).
     if (!thin && tiles(kCfgDma256x256K32P) >= CU) {
         if (!streamk_pays(kCfgDma256x256K32P))
             return kCfgDma256x256K32P;
-        if (K >= 3072 && streamk_pays(kCfgDma128x128K64P))
+        if (K >= 3072 && tiles(kCfgDma256x256K32P) >= 2 * CU && streamk_pays(kCfgDma128x128K64P))
             return kCfgDma256x256K32PSK;
     }
     const int64_t t128 = tiles(kCfgDma128x128K64P);

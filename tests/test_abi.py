@@ -238,9 +238,12 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # 64 x 64 tiles, several per CU
     ((3072, 1024, 2048), "dma_64x64x16_ksplit8_pipe "), ((1900, 1600, 1500), "dma_64x64x32 "),
     ((2176, 2100, 1000), "dma_64x64x32 "),
-    # 400, 576 and 576 128 x 128 tiles, K >= 2048: stream-K over them
+    # 400, 576, 1600 and 1849 128 x 128 tiles, K >= 2048: stream-K over them
+    # (under two rounds of 256 x 256 tiles); 728 256 x 256 tiles with K >=
+    # 3072, 2912 128 x 128 ones: stream-K over the 256 x 256 tiles
     ((2560, 2560, 2560), "dma_128x128x64_pipe_lw2_sk "), ((3072, 3072, 3072), "dma_128x128x64_pipe_lw2_sk "),
-    ((5000, 5000, 5000), "dma_256x256x32_pipe_sk "),
+    ((5000, 5000, 5000), "dma_128x128x64_pipe_lw2_sk "), ((5500, 5500, 3500), "dma_128x128x64_pipe_lw2_sk "),
+    ((7168, 6656, 4096), "dma_256x256x32_pipe_sk "),
     # two or more balanced rounds of 128 x 128 tiles: 16-deep pipelined
     # panels for K < 2048
     ((6000, 2000, 1000), "dma_128x128x16_pipe "), ((4096, 3072, 1024), "dma_128x128x16_pipe "),
