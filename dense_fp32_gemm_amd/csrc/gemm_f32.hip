@@ -64,13 +64,14 @@ struct GemmArgs {
                          // computes a share of their columns with FMAs
     int strip_cols;      // likewise columns N - strip_cols .. N-1, right of
                          // the grid, every workgroup a share of their rows
-                         // (not together with strip_rows)
+                         // above the row strip (which holds the corner)
     int xcds;            // dies the device hands workgroups to round-robin
 };
 
 // Most rows (columns) a remainder strip may hold, and the most columns
 // (rows) of it one workgroup sums.
 constexpr int kMaxStripRows = 4;
+constexpr int kMaxBothStripsK = 3072;   // largest K planned with a row and a column strip
 constexpr int kMaxStripSpread = 8;
 constexpr int kMaxThreads = 1024;      // threads of the largest workgroup
 // LDS floats a strip block's partial sums take (strip_block), at most.
@@ -426,25 +427,25 @@ __device__ inline void poison_region(float *base, int floats, int t, int threads
 }
 
 // One workgroup's block of a remainder strip: C[ar0 + r][bc0 + c] =
-// sum over k of A[ar0 + r][k] * B[k][bc0 + c] for r < nr, c < nc (nr, nc <=
-// kMaxStripSpread), with vector FMAs.  Lane groups of CW threads share a k
-// and take one column each (c = tid % CW, nc <= CW), so a wave's B loads
-// cover 64 / CW rows of CW consecutive columns and its A loads 64 / CW
-// consecutive k of a row.  Thread tid takes k = tid / CW, + NT / CW, ...,
-// loads kBatch of them at a time (one memory latency per batch) and sums
-// them in k order; the NT / CW sums of each output are then added through
+// sum over k of A[ar0 + r][k] * B[k][bc0 + c] for r < nr <= R, c < nc <= CW,
+// with vector FMAs.  Lane groups of CW threads share a k and take one column
+// each (c = tid % CW), so a wave's B loads cover 64 / CW rows of CW
+// consecutive columns and its A loads 64 / CW consecutive k of a row.
+// Thread tid takes k = tid / CW, + NT / CW, ..., loads kBatch = 64 / R of
+// them at a time (one memory latency per batch; R x kBatch A values in
+// registers) and sums them in k order; the NT / CW sums of each output are then added through
 // LDS (`red`, kStripRed floats) in thread order, 16 runs of consecutive
 // threads' sums and then the runs, so the result does not depend on
 // scheduling.  All NT threads call it (it has barriers).  Kept
 // out of line so that the tile kernel around it keeps its registers.
-template <int NT, int CW>
+template <int NT, int CW, int R>
 __device__ __noinline__ void strip_block(const float *A, int64_t lda, const float *B, int64_t ldb, float *C,
                                          int64_t ldc, int K, int ar0, int nr, int bc0, int nc, float *red, int tid)
 {
-    constexpr int R = kMaxStripSpread;
+    static_assert(R <= kMaxStripSpread, "rows of a block");
     constexpr int KS = NT / CW;                // k's one pass covers
     constexpr int PAD = KS + 1;                // sums per output, padded against bank conflicts
-    constexpr int kBatch = 8;                  // k's per thread loaded at once
+    constexpr int kBatch = 64 / R;             // k's per thread loaded at once (R x kBatch A values)
     static_assert(NT % CW == 0 && (R * CW * PAD + 3) / 4 * 4 <= kStripRed, "strip sums fit");
     // A and B are global memory: address them as such (global instead of
     // flat loads).
@@ -1283,34 +1284,38 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         }
 
         // Remainder strips (data-parallel launches only): rows M-R .. M-1
-        // below the tile grid (or columns N-R .. N-1 right of it) are summed
-        // with vector FMAs by every workgroup: the one running tile t takes
-        // w = ceil(N / tiles) of the strip's columns from t * w (of its rows,
-        // ceil(M / tiles) of them), at most kMaxStripSpread, so that no
-        // workgroup streams much of B (A); strip_block sums the block.
+        // below the tile grid and columns N-S .. N-1 right of it (either or
+        // both) are summed with vector FMAs by every workgroup: the one
+        // running tile t takes w = ceil(N / tiles) of the row strip's columns
+        // from t * w, and h = ceil((M - R) / tiles) of the column strip's rows
+        // from t * h, each at most kMaxStripSpread, so that no workgroup
+        // streams much of B (A); the row strip spans all N columns, so the
+        // corner is its.  strip_block sums one block.
         if constexpr (STRIP)
         if (g.strip_rows > 0 || g.strip_cols > 0) {
             const int total = g.tiles_m * g.tiles_n;
-            int ar0, nr, bc0, nc;              // rows ar0 .. of A and C, columns bc0 .. of B and C
+            float *red = &lds[0][0][0];
+            // rows ar0 .. of A and C, columns bc0 .. of B and C
             if (g.strip_rows > 0) {
                 const int w = (g.N + total - 1) / total;
-                ar0 = g.M - g.strip_rows;
-                nr = g.strip_rows;
-                bc0 = t * w;
-                nc = max(0, min(w, g.N - bc0));
-            } else {
-                const int h = (g.M + total - 1) / total;
-                ar0 = t * h;
-                nr = max(0, min(h, g.M - ar0));
-                bc0 = g.N - g.strip_cols;
-                nc = g.strip_cols;
+                const int bc0 = t * w, nc = max(0, min(w, g.N - bc0));
+                __syncthreads();
+                if (nc <= 4)
+                    strip_block<T::kThreads, 4, kMaxStripRows>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K,
+                                                               g.M - g.strip_rows, g.strip_rows, bc0, nc, red, tid);
+                else
+                    strip_block<T::kThreads, 8, kMaxStripRows>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K,
+                                                               g.M - g.strip_rows, g.strip_rows, bc0, nc, red, tid);
             }
-            float *red = &lds[0][0][0];
-            __syncthreads();
-            if (nc <= 4)
-                strip_block<T::kThreads, 4>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K, ar0, nr, bc0, nc, red, tid);
-            else
-                strip_block<T::kThreads, 8>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K, ar0, nr, bc0, nc, red, tid);
+            if (g.strip_cols > 0) {
+                const int rows = g.M - g.strip_rows;
+                const int h = (rows + total - 1) / total;
+                const int ar0 = t * h;
+                __syncthreads();
+                strip_block<T::kThreads, 4, kMaxStripSpread>(g.A, g.lda, g.B, g.ldb, cbase, g.ldc, g.K, ar0,
+                                                             max(0, min(h, rows - ar0)), g.N - g.strip_cols,
+                                                             g.strip_cols, red, tid);
+            }
         }
     };
 
@@ -1939,6 +1944,20 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         strip_rows = M % 64;
         return kCfgDma64x64K16S8P;
     }
+    // Both a last tile row and a last tile column of 1-4 rows (columns):
+    // both as strips, the row strip spanning all N columns, up to K =
+    // kMaxBothStripsK (1025 x 1025 x 1000: 30.7 us against 39.8 for stream-K
+    // over the 4-group K split; 1025 x 1025 x 2000: 47.6 against 54.5 and
+    // 1025 x 1025 x 3000: 66.0 against 71.7 for stream-K over the 8
+    // pipelined groups; but 1025 x 1025 x 4096: 91.4 against 86.9).
+    const int64_t t_inner = (M / 64) * (N / 64);
+    if (K > 512 && K <= kMaxBothStripsK && M % 64 != 0 && M % 64 <= kMaxStripRows && N % 64 != 0 &&
+        N % 64 <= kMaxStripRows && (M % 64) * K <= 4096 && (N % 64) * K <= 4096 && t_inner <= CU && t32 > CU &&
+        ceil_div(N, t_inner) <= kMaxStripSpread && ceil_div(M, t_inner) <= kMaxStripSpread) {
+        strip_rows = M % 64;
+        strip_cols = N % 64;
+        return kCfgDma64x64K16S8P;
+    }
     // The same for a last tile column of at most kMaxStripRows columns.
     const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
     if (K > 512 && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
@@ -2375,11 +2394,13 @@ int gemm_f32_describe(int config, int M, int N, int K, const float *A, int lda,
                                kConfigs[p.config].threads, p.vec_a ? "x4" : "x1", p.vec_b ? "x4" : "x1");
         if (p.strip_rows > 0 && n >= 0 && n < buflen)
             snprintf(buf + n, (size_t)(buflen - n), " strip_rows=%d", p.strip_rows);
-        else if (p.strip_cols > 0 && n >= 0 && n < buflen)
-            snprintf(buf + n, (size_t)(buflen - n), " strip_cols=%d", p.strip_cols);
-        else if (p.wb_c && n >= 0 && n < buflen)
-            snprintf(buf + n, (size_t)(buflen - n), " c_store=write_back");
         int used = (int)strlen(buf);
+        if (p.strip_cols > 0 && used + 1 < buflen)
+            snprintf(buf + used, (size_t)(buflen - used), " strip_cols=%d", p.strip_cols);
+        used = (int)strlen(buf);
+        if (p.wb_c && used + 1 < buflen)
+            snprintf(buf + used, (size_t)(buflen - used), " c_store=write_back");
+        used = (int)strlen(buf);
         if (p.shares_tiles && used + 1 < buflen)
             snprintf(buf + used, (size_t)(buflen - used), " c_accumulate=atomic_add");
         used = (int)strlen(buf);

@@ -220,10 +220,11 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # round of K-split tiles and a strip of FMAs
     ((1025, 1023, 1000), "dma_64x64x16_ksplit8_pipe "), ((1028, 1000, 1000), "dma_64x64x16_ksplit8_pipe "),
     ((1025, 1023, 2048), "dma_64x64x16_ksplit8_pipe "), ((1025, 1023, 3000), "dma_64x64x16_ksplit8_pipe "),
-    ((1023, 1025, 1000), "dma_64x64x16_ksplit8_pipe "),
+    ((1023, 1025, 1000), "dma_64x64x16_ksplit8_pipe "), ((1025, 1025, 1000), "dma_64x64x16_ksplit8_pipe "),
+    ((1025, 1025, 3072), "dma_64x64x16_ksplit8_pipe "),
     # just past one round with K < 1536 (rows x K over 4096): stream-K over
     # the 4-group K split
-    ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "), ((1025, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
+    ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "), ((1029, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
     # 289, 324, 441 and 576 64 x 64 tiles: the idle CU-rounds times K are
     # large enough for stream-K over the 8 pipelined groups.  400 tiles (a
     # last round 56 % full) with K = 1280: two rounds of the 8 groups
@@ -339,21 +340,26 @@ def test_strip_width_never_exceeds_four():
     round of 64 x 64 tiles, where strips are planned, over K from just past
     512 to the strip limit: every planned strip is at most 4 wide, and a
     remainder of 5-63 rows or columns is never a strip."""
-    seen = set()
+    seen, both = set(), set()
     for base_m, base_n in ((1024, 1000), (1000, 1024), (960, 1088), (1088, 960), (1024, 1024)):
         for rem in range(0, 64):
-            for K in (513, 600, 700, 819, 820, 1000, 1023, 1024, 1365, 2047):
-                for M, N in ((base_m + rem, base_n), (base_m, base_n + rem)):
+            for K in (513, 600, 700, 819, 820, 1000, 1023, 1024, 1365, 2047, 3072, 4096):
+                for M, N in ((base_m + rem, base_n), (base_m, base_n + rem), (base_m + rem, base_n + rem % 5)):
                     rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
                     assert rc == gb.GEMM_F32_OK, (M, N, K, text)
-                    m = re.search(r"strip_(rows|cols)=(\d+)", text)
-                    if m:
-                        width = int(m.group(2))
+                    found = re.findall(r"strip_(rows|cols)=(\d+)", text)
+                    for side, width in found:
+                        width = int(width)
                         assert 1 <= width <= 4, (M, N, K, text)
-                        assert width == (M % 64 if m.group(1) == "rows" else N % 64), (M, N, K, text)
-                        seen.add((m.group(1), width))
-    # the sweep does reach strips of every width on both sides
+                        assert width == (M % 64 if side == "rows" else N % 64), (M, N, K, text)
+                        assert width * K <= 4096, (M, N, K, text)
+                        seen.add((side, width))
+                    if len(found) == 2:
+                        assert K <= 3072, (M, N, K, text)
+                        both.add((M % 64, N % 64))
+    # the sweep does reach strips of every width on both sides, and pairs
     assert seen == {(side, w) for side in ("rows", "cols") for w in (1, 2, 3, 4)}, seen
+    assert {(1, 1), (2, 2), (3, 3), (4, 4)} <= both, both
 
 
 def test_sizes_beyond_a_c_int_are_refused_before_the_call():
@@ -379,7 +385,7 @@ def test_sizes_beyond_a_c_int_are_refused_before_the_call():
 def test_describe_names_plans_that_add_into_c():
     """Stream-K plans whose workers split a tile's K-panels sum that tile in C
     with atomic adds (C must be ordinary device memory); describe says so."""
-    rc, text = gb.gemm_f32_describe(-1, 1025, 1025, 1000, FAKE, 1000, FAKE, 1025, FAKE, 1025)
+    rc, text = gb.gemm_f32_describe(-1, 1029, 1025, 1000, FAKE, 1000, FAKE, 1025, FAKE, 1025)
     assert rc == gb.GEMM_F32_OK and "_sk " in text and text.endswith(" c_accumulate=atomic_add"), text
     sk = gb.config_names().index("dma_64x64x64_sk")
     # fewer tiles than workers: one worker per tile, nothing shared

@@ -464,9 +464,14 @@ def test_random_shapes_layouts_and_configs(dev):
 # Stream-K: more tiles than compute units, so the K-panels of some tiles are
 # split between two workgroups that add their partial sums into C.
 # ---------------------------------------------------------------------------
-STREAMK = [("dma_64x64x32_ksplit4_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
+STREAMK = [("dma_64x64x16_ksplit8_pipe_sk", (1025, 1023, 1000)),
+           ("dma_64x64x32_ksplit4_sk", (1025, 1023, 1000)), ("dma_64x64x32_sk", (1100, 1050, 77)),
            ("dma_64x64x64_sk", (1100, 1050, 200)),
            ("dma_64x64x64_sk", (1025, 1023, 1000)),
+           # pieces of 1-5 K-panels for 8 groups (K = 77); a ragged K over two
+           # and three rounds of tiles
+           ("dma_64x64x16_ksplit8_pipe_sk", (1100, 1050, 77)), ("dma_64x64x16_ksplit8_pipe_sk", (1300, 1300, 1003)),
+           ("dma_64x64x16_ksplit8_pipe_sk", (2000, 700, 4100)),
            ("dma_128x128x32_w16_sk", (2176, 2100, 1000)), ("dma_128x128x64_pipe_lw2_sk", (2176, 2100, 1003)),
            ("dma_256x256x32_pipe_sk", (4352, 4200, 203)), ("dma_256x256x32_pipe_sk", (4352, 4200, 200))]
 
@@ -571,7 +576,11 @@ STRIP = [((1025, 1023, 1000), "strip_rows=1"), ((1028, 1000, 1000), "strip_rows=
          ((1025, 1023, 513), "strip_rows=1"), ((1025, 1023, 2047), "strip_rows=1"),
          ((1023, 1025, 2047), "strip_cols=1"), ((1025, 1023, 4096), "strip_rows=1"),
          ((1023, 1025, 4096), "strip_cols=1"), ((1026, 1023, 2048), "strip_rows=2"),
-         ((1025, 1000, 2500), "strip_rows=1")]
+         ((1025, 1000, 2500), "strip_rows=1"),
+         # a row and a column strip (the corner in the row strip), K up to 3072
+         ((1025, 1025, 1000), "strip_rows=1 strip_cols=1"), ((1028, 1025, 1000), "strip_rows=4 strip_cols=1"),
+         ((1025, 1026, 2048), "strip_rows=1 strip_cols=2"), ((1027, 1027, 1300), "strip_rows=3 strip_cols=3"),
+         ((1026, 1028, 1024), "strip_rows=2 strip_cols=4"), ((1025, 1025, 3000), "strip_rows=1 strip_cols=1")]
 
 
 @pytest.mark.parametrize("shape,strip", STRIP, ids=["x".join(map(str, s)) for s, _ in STRIP])
