@@ -189,8 +189,8 @@ GEMM_F32_API int gemm_f32_config_info(int config, int *bm, int *bn, int *bk,
  * these arguments (config -1: what gemm_f32() would enqueue): the
  * configuration name first ("none" for an empty output, "fill_zero" for
  * K == 0), then tile grid, workgroup count and load widths, and, when the
- * last 1-4 rows or columns are computed as a strip beside the tile grid,
- * " strip_rows=R" or " strip_cols=C"; when C has at least 2^23 elements and
+ * last 1-4 rows or columns (or both) are computed as strips beside the tile
+ * grid, " strip_rows=R" and/or " strip_cols=C"; when C has at least 2^23 elements and
  * rows that are not 16-byte aligned (C's address or ldc * 4 not a multiple
  * of 16) and the configuration has such a variant, " c_store=write_back"
  * (C written with ordinary rather than streaming stores); last, when a
