@@ -1900,9 +1900,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         // K, from K = 1024 on with two or more tiles per CU; otherwise four
         // or more 64 x 64 tiles per CU balance well enough (2200 x 2200 x
         // 1500, 324 tiles: 135 us against 148 for stream-K; 941 x 4305 x
-        // 1100, 272: 81 against 107).
+        // 1100, 272: 81 against 107), unless with K >= 1024 the last round
+        // of 128 x 128 tiles is over four fifths full: two rounds of the
+        // 32-deep pipelined tile (3428 x 2297 x 1956, 486 tiles: 235 us
+        // against 267 for 64 x 64 tiles).
         if (K >= 2048 || (K >= 1024 && t128 >= 2 * CU))
             return deep_ok ? kCfgDma128x128K64PSK : kCfgDma128x128K32W16SK;
+        if (K >= 1024 && t128 <= 2 * CU && !unbalanced(kCfgDma128x128K64P))
+            return kCfgDma128x128K32P;
         return kCfgDma64x64K32;
     }
     // At least three quarters of the CUs busy with 128 x 128 tiles: one
@@ -1970,6 +1975,17 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         const int64_t k4 = 32 * ceil_div(K, 32);                  // K the loader-wave tile covers
         return K >= 1536 || (K >= 640 && 8 * k8 <= 9 * k4) ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
     }
+    // Past one round, 32 x 64 (64 x 32) tiles of the 8 one-wave K-split
+    // groups that fill at most two rounds (a last tile row of at most 32
+    // rows) give no CU more work than one round of 64 x 64 tiles would; up
+    // to K = 2560 that beats stream-K (535 x 1913 x 2314: 53.0 us against
+    // 60.0 for stream-K over the 8 pipelined groups; 1620 x 634 x 695: 22.1
+    // against 30.4 for stream-K over the 4-group K split; 4157 x 207 x 1519:
+    // 38.4 against 44.1; but 1247 x 792 x 4980: 99.2 against 91.1).
+    if (K > 512 && K < 2560 && tiles(kCfgDma32x64K16S8) <= 2 * CU)
+        return kCfgDma32x64K16S8;
+    if (K > 512 && K < 2560 && tiles(kCfgDma64x32K16S8) <= 2 * CU)
+        return kCfgDma64x32K16S8;
     // Past one round, a side under 192 that 64-wide tiles pad a third more
     // than 32-wide ones: 32 x 64 (64 x 32) tiles of the 8 one-wave K-split
     // groups, in up to three rounds, do less work (95 x 8926 x 1248: 32.5 us

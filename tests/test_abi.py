@@ -266,6 +266,14 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((15133, 90, 3196), "dma_64x32x16_ksplit8 "),
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe_lw2 "),
+    # past one round of 64 x 64 tiles, 32 x 64 (64 x 32) ones that fill at
+    # most two rounds, for K < 2560; stream-K over the 8 pipelined groups
+    # from there
+    ((535, 1913, 2314), "dma_32x64x16_ksplit8 "), ((4157, 207, 1519), "dma_64x32x16_ksplit8 "),
+    ((1620, 634, 695), "dma_32x64x16_ksplit8 "), ((1247, 792, 4980), "dma_64x64x16_ksplit8_pipe_sk "),
+    # 486 128 x 128 tiles (a second round 90 % full) with 1024 <= K < 2048:
+    # two rounds of the 32-deep pipelined tile; 324 (27 % full): 64 x 64
+    ((3428, 2297, 1956), "dma_128x128x32_pipe "), ((2200, 2200, 1500), "dma_64x64x32 "),
 ])
 def test_selection(shape, name):
     M, N, K = shape
