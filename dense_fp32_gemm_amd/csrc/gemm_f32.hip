@@ -1911,14 +1911,17 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         return kCfgDma64x64K32;
     }
     // At least three quarters of the CUs busy with 128 x 128 tiles: one
-    // round of them if 64 x 64 tiles would leave their last round mostly
-    // idle; with four fifths busy and K >= 2048 also otherwise, the bigger
-    // tiles' efficiency outweighing the idle CUs (2372 x 1619 x 7588, 247
+    // round of them where 64 x 64 tiles would take four rounds, as much
+    // work per CU, the bigger tiles doing it faster (2372 x 1619 x 7588, 247
     // tiles: 443 us against 504 for 64 x 64 tiles; 1746 x 1863 x 3494, 210:
-    // 211 against 235; but 3072 x 1024 x 2048, 192: 126 against 109).
-    if (!thin && deep_ok && K > 512 && 4 * t128 >= 3 * CU &&
-        (unbalanced(kCfgDma64x64K32) || (K >= 2048 && 5 * t128 >= 4 * CU)))
-        return kCfgDma128x128K64P;
+    // 211 against 235; 3394 x 1064 x 960, 918 64 x 64 tiles: 62.9 against
+    // 69.5; but 3072 x 1024 x 2048, 192 (768): 126 against 109; 1551 x 1838
+    // x 1619, 195 (725): 104.6 against 88.3); the loader-wave tile's 64-deep
+    // panels unless the last one would be at most half used, then 32-deep
+    // ones (2286 x 1396 x 758: 53.6 us against 54.0; 2282 x 1391 x 771: 57.6
+    // against 60.1).
+    if (!thin && K > 512 && 4 * t128 >= 3 * CU && ceil_div(tiles(kCfgDma64x64K32), CU) >= 4)
+        return deep_ok && 64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) ? kCfgDma128x128K64P : kCfgDma128x128K32P;
     // 64 x 64 tiles with K > 512, up to three rounds of them.  One tile per
     // CU: 8 pipelined one-wave K-split groups from K = 640 on, unless the
     // 16-deep panels split unevenly over the groups (the busiest group's
@@ -2007,13 +2010,18 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 2414 x 2779, 94 % full: 142 against 141, and 3280 x 682 x 1149, 75 %:
     // 66.6 against 64.4 for 64 x 64 tiles), except just past one round with
     // K < 1536, where the 4-group K split's lighter pieces win (574 x 1850 x
-    // 1256: 40.6 us against 43.0).
+    // 1256: 40.6 us against 43.0), and below K = 1150 32 x 32 tiles of 4
+    // one-wave K-split groups, two workgroups per CU, without stream-K's
+    // extra launch (660 x 1684 x 979: 35.6 us against 38.3; 789 x 1518 x
+    // 1137: 40.6 against 43.7; on 10 random shapes of 257-320 64 x 64 tiles
+    // with K in 513-950: 0.1 % above the per-shape best, against 10 % for
+    // stream-K; but 1993 x 539 x 1078: 39.8 against 39.4).
     const int64_t rounds = ceil_div(t32, CU);
     if (K >= 950 && t32 <= 3 * CU && (rounds * CU - t32) * K >= 320 * rounds * CU &&
         (t32 > 5 * CU / 4 || K >= 1536))
         return kCfgDma64x64K16S8PSK;
     if (K > 512 && t32 <= 5 * CU / 4)
-        return kCfgDma64x64K32S4SK;
+        return K < 1150 ? kCfgDma32x32K32S4 : kCfgDma64x64K32S4SK;
     // Two rounds favour the 8 pipelined groups from K = 1024 on (2048 x
     // 1024 x 1024: 39.3 us against 42.1 for 64 x 64 tiles of 4 waves; 1600
     // x 1200 x 1200: 45.2 against 48.5; 2048 x 1024 x 1100: 45.5 against

@@ -224,7 +224,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1025, 1025, 3072), "dma_64x64x16_ksplit8_pipe "),
     # just past one round with K < 1536 (rows x K over 4096): stream-K over
     # the 4-group K split
-    ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "), ((1029, 1025, 1000), "dma_64x64x32_ksplit4_sk "),
+    ((1028, 1000, 1500), "dma_64x64x32_ksplit4_sk "), ((1029, 1025, 1200), "dma_64x64x32_ksplit4_sk "),
     # 289, 324, 441 and 576 64 x 64 tiles: the idle CU-rounds times K are
     # large enough for stream-K over the 8 pipelined groups.  400 tiles (a
     # last round 56 % full) with K = 1280: two rounds of the 8 groups
@@ -271,6 +271,15 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # from there
     ((535, 1913, 2314), "dma_32x64x16_ksplit8 "), ((4157, 207, 1519), "dma_64x32x16_ksplit8 "),
     ((1620, 634, 695), "dma_32x64x16_ksplit8 "), ((1247, 792, 4980), "dma_64x64x16_ksplit8_pipe_sk "),
+    # just past one round of 64 x 64 tiles with K < 1150: 32 x 32 tiles of 4
+    # K-split groups
+    ((309, 3485, 597), "dma_32x32x32_ksplit4 "), ((660, 1684, 979), "dma_32x32x32_ksplit4 "),
+    ((574, 1850, 1256), "dma_64x64x32_ksplit4_sk "),
+    # 198-249 128 x 128 tiles where 64 x 64 tiles take four rounds: one
+    # round of 128 x 128, 32-deep panels if a 64-deep last one would be at
+    # most half used; three rounds of 64 x 64 tiles: those
+    ((3394, 1064, 960), "dma_128x128x64_pipe_lw2 "), ((2282, 1391, 771), "dma_128x128x32_pipe "),
+    ((1551, 1838, 1619), "dma_64x64x32 "), ((3072, 1024, 2048), "dma_64x64x16_ksplit8_pipe "),
     # 486 128 x 128 tiles (a second round 90 % full) with 1024 <= K < 2048:
     # two rounds of the 32-deep pipelined tile; 324 (27 % full): 64 x 64
     ((3428, 2297, 1956), "dma_128x128x32_pipe "), ((2200, 2200, 1500), "dma_64x64x32 "),
@@ -393,7 +402,7 @@ def test_sizes_beyond_a_c_int_are_refused_before_the_call():
 def test_describe_names_plans_that_add_into_c():
     """Stream-K plans whose workers split a tile's K-panels sum that tile in C
     with atomic adds (C must be ordinary device memory); describe says so."""
-    rc, text = gb.gemm_f32_describe(-1, 1029, 1025, 1000, FAKE, 1000, FAKE, 1025, FAKE, 1025)
+    rc, text = gb.gemm_f32_describe(-1, 1029, 1025, 1200, FAKE, 1200, FAKE, 1025, FAKE, 1025)
     assert rc == gb.GEMM_F32_OK and "_sk " in text and text.endswith(" c_accumulate=atomic_add"), text
     sk = gb.config_names().index("dma_64x64x64_sk")
     # fewer tiles than workers: one worker per tile, nothing shared

@@ -59,5 +59,5 @@ def test_plans_are_sized_from_the_device(cuda):
     """Stream-K runs one worker per compute unit of the current device."""
     cus = cuda.cuda.get_device_properties(0).multi_processor_count
     fake = 0x100000
-    rc, text = gb.gemm_f32_describe(-1, 1029, 1025, 1000, fake, 1000, fake, 1025, fake, 1025)
+    rc, text = gb.gemm_f32_describe(-1, 1029, 1025, 1200, fake, 1200, fake, 1025, fake, 1025)
     assert rc == gb.GEMM_F32_OK and f" grid={cus} " in text, text
