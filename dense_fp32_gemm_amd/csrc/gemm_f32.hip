@@ -1761,8 +1761,9 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //  * at least one 256 x 256 tile per CU: 256 x 256 with 4 software-pipelined
 //    waves of 128 x 128, 32-deep panels, if they fill their rounds (8192^3:
 //    7.31 ms against 7.45 for 16 waves of 64 x 64; 4096 x 4096 x 16384: 3.66
-//    against 3.72); their stream-K twin for K >= 3072 if 128 x 128 tiles
-//    would not fill their rounds either (5000^3: 1832 us against 2381);
+//    against 3.72); their stream-K twin for K >= 3072 with two or more
+//    rounds of them if 128 x 128 tiles would not fill their rounds either
+//    (7168 x 6656 x 4096: 2649 us against 2676 for the 128 x 128 twin);
 //  * at least one 128 x 128 tile per CU, rounds filled: 128 x 128 with 4
 //    pipelined waves of 64 x 64 -- one round: 64-deep panels fed by two
 //    loader waves (2048^3: 123 us against 125.6 when the MFMA waves load,
@@ -1771,12 +1772,13 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    16-deep panels, three workgroups per CU (6144 x 2048 x 4096: 717
 //    against 727); rounds not filled: the loader-wave tile's stream-K twin
 //    for K >= 2048, or K >= 1024 with two or more tiles per CU (3072^3: 428
-//    us against 455 for 64 x 64); otherwise, and for one or two rounds with
-//    K < 512, 64 x 64 tiles;
-//  * at least three quarters of the CUs busy with 128 x 128 tiles while
-//    64 x 64 tiles would leave the last round mostly idle, or four fifths
-//    busy with K >= 2048: one round of the loader-wave 128 x 128 tile
-//    (1792^3: 109 us against 121 for 64 x 64);
+//    us against 455 for 64 x 64), two rounds of the 32-deep tile for K >=
+//    1024 with a second round over four fifths full; otherwise, and for one
+//    or two rounds with K < 512, 64 x 64 tiles;
+//  * at least three quarters of the CUs busy with 128 x 128 tiles where
+//    64 x 64 tiles would take four rounds: one round of the loader-wave
+//    128 x 128 tile (1792^3: 109 us against 121 for 64 x 64), of the
+//    32-deep one if a 64-deep last panel would be at most half used;
 //  * at most one 64 x 64 tile per CU with K > 512 (mid-size squares, skinny
 //    shapes): from K = 640 on, K split over 8 software-pipelined one-wave
 //    groups (16384 x 64 x 4096: 72 us against 79 for 4 groups of 4 waves;
@@ -1784,13 +1786,17 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    K < 1536 and its 16-deep panels split unevenly over the 8 groups; else
 //    4 pipelined waves of 32 x 32 fed by two loader waves through four
 //    32-deep panels (1000 x 1000 x 600: 17.6 us against 18.1); a last tile row
-//    (column) of 1-4 rows (columns) past one round: one round of the 4-group
-//    K-split tile, the remainder computed as a strip;
+//    (column, or both) of 1-4 rows (columns) past one round: one round of
+//    the 8 pipelined groups, the remainder computed as strips spread over
+//    all workgroups; past one round, 32 x 64 (64 x 32) tiles of 8 one-wave
+//    K-split groups where they fill at most two rounds (K < 2560) or where
+//    64-wide tiles would pad a side under 192 by a third more;
 //  * up to three rounds of 64 x 64 tiles, K >= 950 and idle CU-rounds x K
 //    large enough: stream-K over the 8 pipelined groups (1536^3: 70 us
 //    against 82 for stream-K over 4 groups; 1025 x 1025 x 4096: 87 against
 //    104), over the 4-group K split instead just past one round with K <
-//    1536; otherwise two rounds with K >= 1024, or three with K >= 2048:
+//    1536 (32 x 32 tiles of 4 K-split groups below K = 1150); otherwise two
+//    rounds with K >= 1024, or three with K >= 2048:
 //    whole tiles of the 8 pipelined groups (1300 x 1300 x 4096: 136 us
 //    against 149; 2048 x 1536 x 2048: 101 against 110);
 //  * otherwise 64-row or 64-column tiles if there are at least two per CU,
