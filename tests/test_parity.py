@@ -461,6 +461,34 @@ def test_random_shapes_layouts_and_configs(dev):
 
 
 # ---------------------------------------------------------------------------
+# The shape rule's branches, one shape each, through the automatic plan
+# (config -1): the plan is the expected one and its C is the oracle's, bit
+# for bit, on quarter-step operands, with C's row padding untouched.
+# ---------------------------------------------------------------------------
+RULE_BRANCHES = [((535, 1913, 700), "dma_32x64x16_ksplit8 "),         # two rounds of 32 x 64
+                 ((1913, 535, 700), "dma_64x32x16_ksplit8 "),         # two rounds of 64 x 32
+                 ((660, 1684, 979), "dma_32x32x32_ksplit4 "),         # just past one round, K < 1150
+                 ((1100, 1100, 1100), "dma_64x64x16_ksplit8_pipe_sk "),
+                 ((1197, 2414, 2200), "dma_64x64x16_ksplit8_pipe "),  # three fuller rounds
+                 ((2282, 1391, 771), "dma_128x128x32_pipe "),         # one round of 128 x 128, 32-deep
+                 ((3394, 1064, 960), "dma_128x128x64_pipe_lw2 "),     # the same, 64-deep
+                 ((3428, 2297, 1100), "dma_128x128x32_pipe "),        # a nearly full second round
+                 ((1025, 1025, 2000), "dma_64x64x16_ksplit8_pipe ")]  # row and column strips
+
+
+@pytest.mark.parametrize("shape,name", RULE_BRANCHES, ids=["x".join(map(str, s)) for s, _ in RULE_BRANCHES])
+def test_rule_branches_bit_exact(dev, shape, name):
+    M, N, K = shape
+    rc, desc = gb.gemm_f32_describe(-1, M, N, K, 16, K, 16, N, 16, N + 3)
+    assert rc == gb.GEMM_F32_OK and desc.startswith(name), desc
+    A, B = operands("quarter", M, N, K)
+    got, full = gpu_gemm(A, B, -1, dev, pad=(0, 0, 3))
+    assert_bit_exact(got, oracle.gemm(A, B), f"{shape} {desc}")
+    body = full[:M * (N + 3)].reshape(M, N + 3)
+    assert np.isnan(body[:, N:]).all() and np.isnan(full[M * (N + 3):]).all()
+
+
+# ---------------------------------------------------------------------------
 # Stream-K: more tiles than compute units, so the K-panels of some tiles are
 # split between two workgroups that add their partial sums into C.
 # ---------------------------------------------------------------------------
