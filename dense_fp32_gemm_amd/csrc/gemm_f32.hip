@@ -1337,10 +1337,9 @@ __global__ __launch_bounds__(T::kThreads) void gemm_f32_mfma_dma(GemmArgs g)
         const int first = (int)((lo + ktiles - 1) / ktiles);   // first tile starting at or after lo
         const int last = (int)(hi / ktiles);                    // tile holding panel hi (or one past)
         const int p_lo = (int)(lo % ktiles), p_hi = (int)(hi % ktiles);
-        if (lo >= hi) {
-        } else if (first > last) {
+        if (lo < hi && first > last) {
             work(last, p_lo, p_hi);                             // inside one tile
-        } else {
+        } else if (lo < hi) {
             for (int t = first; t < last; ++t)
                 work(t, 0, ktiles);
             if (p_hi > 0)
