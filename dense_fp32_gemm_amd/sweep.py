@@ -61,13 +61,15 @@ def sweep_shape(torch, shape, configs, steps, warmup, log=print):
     if rc != gb.GEMM_F32_OK or not bool(torch.isfinite(ref).all()):
         raise RuntimeError(f"reference kernel failed on {shape}: {gb.gemm_f32_status_string(rc)}")
     # The automatic plan (config -1) runs as a candidate of its own: it can
-    # differ from every forced configuration (a remainder strip).
+    # differ from every forced configuration (a remainder strip).  It is
+    # checked and timed first, so that no slow forced configuration runs
+    # just before it.
     _, plan = gb.gemm_f32_describe(-1, M, N, K, A.data_ptr(), K, B.data_ptr(), N, C.data_ptr(), N)
     strip = [w for w in plan.split() if w.startswith("strip_")]
     names = {c: gb.gemm_f32_config_name(c) for c in configs}
     names[-1] = "auto:" + (plan.split() or ["?"])[0] + "".join(" " + w for w in strip)
     passed = []
-    for c in list(configs) + [-1]:
+    for c in [-1] + list(configs):
         C.fill_(float("nan"))
         rc = _run(torch, c, A, B, C, stream)
         torch.cuda.synchronize()
