@@ -500,6 +500,9 @@ STREAMK = [("dma_64x64x16_ksplit8_pipe_sk", (1025, 1023, 1000)),
            # and three rounds of tiles
            ("dma_64x64x16_ksplit8_pipe_sk", (1100, 1050, 77)), ("dma_64x64x16_ksplit8_pipe_sk", (1300, 1300, 1003)),
            ("dma_64x64x16_ksplit8_pipe_sk", (2000, 700, 4100)),
+           # ranges of about 2.9 and 3.4 tiles: two or three whole tiles
+           # before each workgroup's start and end pieces
+           ("dma_64x64x16_ksplit8_pipe_sk", (1252, 2307, 600)), ("dma_128x128x64_pipe_lw2_sk", (4500, 3000, 520)),
            ("dma_128x128x32_w16_sk", (2176, 2100, 1000)), ("dma_128x128x64_pipe_lw2_sk", (2176, 2100, 1003)),
            ("dma_256x256x32_pipe_sk", (4352, 4200, 203)), ("dma_256x256x32_pipe_sk", (4352, 4200, 200))]
 
