@@ -1944,15 +1944,17 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // A last tile row of at most kMaxStripRows rows that alone takes the
     // tiles past one round: those rows become a strip computed with FMAs,
     // spread over all workgroups, and the rest runs as one round of the 8
-    // pipelined K-split groups.  Strips stay up to rows x K = 4096, and each
-    // workgroup's share of the strip's columns up to kMaxStripSpread
-    // (1025 x 1023 x 1000: 26.8 us against 29.7 for the strip summed by the
-    // last tile row of 4-group K-split tiles, 37.3 for stream-K; 1000 x 1028
-    // x 1000: 26.7 against 35.0; 1025 x 1023 x 3000: 58.2 against 65.2 for
-    // stream-K over the 8 pipelined groups).
+    // pipelined K-split groups.  Strips stay from K = 257 up to rows x K =
+    // 4096, and each workgroup's share of the strip's columns up to
+    // kMaxStripSpread (1025 x 1023 x 1000: 26.8 us against 29.7 for the
+    // strip summed by the last tile row of 4-group K-split tiles, 37.3 for
+    // stream-K; 1000 x 1028 x 1000: 26.7 against 35.0; 1025 x 1023 x 3000:
+    // 58.2 against 65.2 for stream-K over the 8 pipelined groups; 1028 x 1000
+    // x 400: 17.3 against 20.7 for two rounds of 64 x 64 tiles; but 1023 x
+    // 1025 x 256: 15.3 against 15.3).
     const int64_t t_full = (M / 64) * ceil_div(N, 64);
     static_assert(std::is_same<Tile64x64K16S8P, StripTile>::value, "the strip tile is the 8-group pipelined K split");
-    if (K > 512 && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
+    if (K > 256 && M % 64 != 0 && M % 64 <= kMaxStripRows && (M % 64) * K <= 4096 &&
         t_full <= CU && t32 > CU && ceil_div(N, t_full) <= kMaxStripSpread) {
         strip_rows = M % 64;
         return kCfgDma64x64K16S8P;
@@ -1964,7 +1966,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 1025 x 1025 x 3000: 66.0 against 71.7 for stream-K over the 8
     // pipelined groups; but 1025 x 1025 x 4096: 91.4 against 86.9).
     const int64_t t_inner = (M / 64) * (N / 64);
-    if (K > 512 && K <= kMaxBothStripsK && M % 64 != 0 && M % 64 <= kMaxStripRows && N % 64 != 0 &&
+    if (K > 256 && K <= kMaxBothStripsK && M % 64 != 0 && M % 64 <= kMaxStripRows && N % 64 != 0 &&
         N % 64 <= kMaxStripRows && (M % 64) * K <= 4096 && (N % 64) * K <= 4096 && t_inner <= CU && t32 > CU &&
         ceil_div(N, t_inner) <= kMaxStripSpread && ceil_div(M, t_inner) <= kMaxStripSpread) {
         strip_rows = M % 64;
@@ -1973,7 +1975,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     }
     // The same for a last tile column of at most kMaxStripRows columns.
     const int64_t t_full_n = ceil_div(M, 64) * (N / 64);
-    if (K > 512 && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
+    if (K > 256 && N % 64 != 0 && N % 64 <= kMaxStripRows && (N % 64) * K <= 4096 &&
         t_full_n <= CU && t32 > CU && ceil_div(M, t_full_n) <= kMaxStripSpread) {
         strip_cols = N % 64;
         return kCfgDma64x64K16S8P;

@@ -179,7 +179,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x16_ksplit8_pipe_sk "), text
     rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 1000, FAKE, 1000, FAKE, ldb, FAKE, 1023)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x16_ksplit8_pipe ") and "strip_rows=1" in text, text
-    rc, text = gb.gemm_f32_describe(-1, 1025, 1023, 500, FAKE, 500, FAKE, ldb, FAKE, 1023)
+    rc, text = gb.gemm_f32_describe(-1, 1023, 1025, 256, FAKE, 256, FAKE, ldb, FAKE, 1025)
     assert rc == gb.GEMM_F32_OK and text.startswith("dma_64x64x32 "), text
     k64 = gb.config_names().index("dma_64x64x64")
     rc, _ = gb.gemm_f32_describe(k64, 1024, 1024, 1024, FAKE, 1024, FAKE, ldb, FAKE, 1024)
@@ -231,7 +231,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1025, 1025, 4096), "dma_64x64x16_ksplit8_pipe_sk "),
     ((1100, 1100, 1100), "dma_64x64x16_ksplit8_pipe_sk "), ((1300, 1300, 4096), "dma_64x64x16_ksplit8_pipe_sk "),
     ((1536, 1536, 1536), "dma_64x64x16_ksplit8_pipe_sk "), ((1280, 1280, 1280), "dma_64x64x16_ksplit8_pipe "),
-    ((1025, 1023, 300), "dma_64x64x64 "), ((1590, 744, 100), "dma_64x64x32 "),
+    ((1025, 1023, 300), "dma_64x64x16_ksplit8_pipe "), ((1023, 1025, 256), "dma_64x64x64 "),
+    ((1590, 744, 100), "dma_64x64x32 "),
     # two balanced rounds: the pipelined K split for K >= 1024, else 64 x 64
     ((2048, 1024, 1024), "dma_64x64x16_ksplit8_pipe "),
     ((1400, 1400, 1000), "dma_64x64x64 "), ((2048, 1024, 768), "dma_64x64x64 "),
@@ -360,7 +361,7 @@ def test_strip_width_never_exceeds_four():
     seen, both = set(), set()
     for base_m, base_n in ((1024, 1000), (1000, 1024), (960, 1088), (1088, 960), (1024, 1024)):
         for rem in range(0, 64):
-            for K in (513, 600, 700, 819, 820, 1000, 1023, 1024, 1365, 2047, 3072, 4096):
+            for K in (256, 257, 400, 513, 600, 700, 819, 820, 1000, 1023, 1024, 1365, 2047, 3072, 4096):
                 for M, N in ((base_m + rem, base_n), (base_m, base_n + rem), (base_m + rem, base_n + rem % 5)):
                     rc, text = gb.gemm_f32_describe(-1, M, N, K, FAKE, K, FAKE, N, FAKE, N)
                     assert rc == gb.GEMM_F32_OK, (M, N, K, text)

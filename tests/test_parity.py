@@ -611,7 +611,10 @@ STRIP = [((1025, 1023, 1000), "strip_rows=1"), ((1028, 1000, 1000), "strip_rows=
          # a row and a column strip (the corner in the row strip), K up to 3072
          ((1025, 1025, 1000), "strip_rows=1 strip_cols=1"), ((1028, 1025, 1000), "strip_rows=4 strip_cols=1"),
          ((1025, 1026, 2048), "strip_rows=1 strip_cols=2"), ((1027, 1027, 1300), "strip_rows=3 strip_cols=3"),
-         ((1026, 1028, 1024), "strip_rows=2 strip_cols=4"), ((1025, 1025, 3000), "strip_rows=1 strip_cols=1")]
+         ((1026, 1028, 1024), "strip_rows=2 strip_cols=4"), ((1025, 1025, 3000), "strip_rows=1 strip_cols=1"),
+         # K from 257 on
+         ((1028, 1000, 400), "strip_rows=4"), ((1023, 1026, 257), "strip_cols=2"),
+         ((1025, 1025, 300), "strip_rows=1 strip_cols=1")]
 
 
 @pytest.mark.parametrize("shape,strip", STRIP, ids=["x".join(map(str, s)) for s, _ in STRIP])
