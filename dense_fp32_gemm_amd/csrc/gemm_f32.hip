@@ -1987,14 +1987,16 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     }
     // Past one round, 32 x 64 (64 x 32) tiles of the 8 one-wave K-split
     // groups that fill at most two rounds (a last tile row of at most 32
-    // rows) give no CU more work than one round of 64 x 64 tiles would; up
-    // to K = 2560 that beats stream-K (535 x 1913 x 2314: 53.0 us against
-    // 60.0 for stream-K over the 8 pipelined groups; 1620 x 634 x 695: 22.1
-    // against 30.4 for stream-K over the 4-group K split; 4157 x 207 x 1519:
-    // 38.4 against 44.1; but 1247 x 792 x 4980: 99.2 against 91.1).
-    if (K > 512 && K < 2560 && tiles(kCfgDma32x64K16S8) <= 2 * CU)
+    // rows) give no CU more work than one round of 64 x 64 tiles would; for
+    // 256 < K < 2560 that beats stream-K and a second round of 64 x 64 tiles
+    // (535 x 1913 x 2314: 53.0 us against 60.0 for stream-K over the 8
+    // pipelined groups; 1620 x 634 x 695: 22.1 against 30.4 for stream-K
+    // over the 4-group K split; 4157 x 207 x 1519: 38.4 against 44.1; 535 x
+    // 1913 x 450: 18.7 against 22.6 for dma_64x64x32; but 1247 x 792 x 4980:
+    // 99.2 against 91.1).
+    if (K > 256 && K < 2560 && t32 > CU && tiles(kCfgDma32x64K16S8) <= 2 * CU)
         return kCfgDma32x64K16S8;
-    if (K > 512 && K < 2560 && tiles(kCfgDma64x32K16S8) <= 2 * CU)
+    if (K > 256 && K < 2560 && t32 > CU && tiles(kCfgDma64x32K16S8) <= 2 * CU)
         return kCfgDma64x32K16S8;
     // Past one round, a side under 192 that 64-wide tiles pad a third more
     // than 32-wide ones: 32 x 64 (64 x 32) tiles of the 8 one-wave K-split

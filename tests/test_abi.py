@@ -268,9 +268,11 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # 196 128 x 128 tiles against 784 64 x 64 ones (a fourth round barely used)
     ((1792, 1792, 1792), "dma_128x128x64_pipe_lw2 "),
     # past one round of 64 x 64 tiles, 32 x 64 (64 x 32) ones that fill at
-    # most two rounds, for K < 2560; stream-K over the 8 pipelined groups
-    # from there
+    # most two rounds, for 256 < K < 2560; stream-K over the 8 pipelined
+    # groups from there, two rounds of 64 x 64 tiles below
     ((535, 1913, 2314), "dma_32x64x16_ksplit8 "), ((4157, 207, 1519), "dma_64x32x16_ksplit8 "),
+    ((535, 1913, 450), "dma_32x64x16_ksplit8 "), ((535, 1913, 256), "dma_64x64x64 "),
+    ((1000, 1000, 300), "dma_64x64x64 "),
     ((1620, 634, 695), "dma_32x64x16_ksplit8 "), ((1247, 792, 4980), "dma_64x64x16_ksplit8_pipe_sk "),
     # just past one round of 64 x 64 tiles with K < 1150: 32 x 32 tiles of 4
     # K-split groups
