@@ -1927,8 +1927,9 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // against 60.1).
     if (!thin && K > 512 && 4 * t128 >= 3 * CU && ceil_div(tiles(kCfgDma64x64K32), CU) >= 4)
         return deep_ok && 64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) ? kCfgDma128x128K64P : kCfgDma128x128K32P;
-    // 64 x 64 tiles with K > 512, up to three rounds of them.  One tile per
-    // CU: 8 pipelined one-wave K-split groups from K = 640 on, unless the
+    // 64 x 64 tiles with K > 512 (one round: K >= 400), up to three rounds
+    // of them.  One tile per CU: 8 pipelined one-wave K-split groups from K
+    // = 640 on (and from 400 to 512), unless the
     // 16-deep panels split unevenly over the groups (the busiest group's
     // rounds span over 9/8 of K rounded up to 32-deep panels) while K < 1536;
     // otherwise 4 pipelined waves of 32 x 32 fed by two loader waves through
@@ -1980,10 +1981,15 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         strip_cols = N % 64;
         return kCfgDma64x64K16S8P;
     }
-    if (K > 512 && t32 <= CU) {
+    // (From K = 400 to 512 the 8 groups win whatever the split: 1024 x 1024
+    // x 512: 14.1 us against 16.2 for dma_64x64x64; 1024 x 1024 x 448: 13.3
+    // against 14.3 for the loader-wave tile; 1000 x 1000 x 400: 13.9 against
+    // 14.9;
+    // below, 64 x 64 tiles of 4 waves: 1024 x 1024 x 300: 12.2 against 12.5.)
+    if (K >= 400 && t32 <= CU) {
         const int64_t k8 = 128 * ceil_div(ceil_div(K, 16), 8);   // K the busiest of the 8 groups covers
         const int64_t k4 = 32 * ceil_div(K, 32);                  // K the loader-wave tile covers
-        return K >= 1536 || (K >= 640 && 8 * k8 <= 9 * k4) ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
+        return K <= 512 || K >= 1536 || (K >= 640 && 8 * k8 <= 9 * k4) ? kCfgDma64x64K16S8P : kCfgDma64x64K32PL2S4;
     }
     // Past one round, 32 x 64 (64 x 32) tiles of the 8 one-wave K-split
     // groups that fill at most two rounds (a last tile row of at most 32

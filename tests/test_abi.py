@@ -201,6 +201,8 @@ def test_wide_rows_fall_back_to_staged_kernels():
     ((1024, 1024, 1536), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 1535), "dma_64x64x16_ksplit8_pipe "),
     ((1000, 1000, 1000), "dma_64x64x16_ksplit8_pipe "), ((768, 768, 1024), "dma_64x64x16_ksplit8_pipe "),
     ((1024, 1024, 640), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 700), "dma_64x64x16_ksplit8_pipe "),
+    ((1024, 1024, 512), "dma_64x64x16_ksplit8_pipe "), ((1000, 1000, 400), "dma_64x64x16_ksplit8_pipe "),
+    ((960, 1000, 350), "dma_64x64x32 "),
     ((800, 1200, 650), "dma_64x64x32_pipe_lw2_s4 "), ((1000, 1000, 639), "dma_64x64x32_pipe_lw2_s4 "),
     ((1000, 1000, 600), "dma_64x64x32_pipe_lw2_s4 "), ((1000, 1000, 513), "dma_64x64x32_pipe_lw2_s4 "),
     # K <= 512: no K split; 64-deep panels unless the last one would be at
