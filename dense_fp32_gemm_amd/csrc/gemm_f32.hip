@@ -1790,7 +1790,7 @@ bool dma_offsets_fit(const ConfigInfo &c, int64_t lda, int64_t ldb)
 //    all workgroups; past one round, 32 x 64 (64 x 32) tiles of 8 one-wave
 //    K-split groups where they fill at most two rounds (K < 2560) or where
 //    64-wide tiles would pad a side under 192 by a third more;
-//  * up to three rounds of 64 x 64 tiles, K >= 950 and idle CU-rounds x K
+//  * up to six rounds of 64 x 64 tiles, K >= 950 and idle CU-rounds x K
 //    large enough: stream-K over the 8 pipelined groups (1536^3: 70 us
 //    against 82 for stream-K over 4 groups; 1025 x 1025 x 4096: 87 against
 //    104), over the 4-group K split instead just past one round with K <
@@ -1855,6 +1855,13 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         const int64_t t = tiles(c);
         return K >= 1024 ? 25 * t < 24 * ceil_div(t, CU) * CU : unbalanced(c);
     };
+    // Stream-K over the 8 pipelined groups of 64 x 64 tiles (below) pays
+    // where, with up to max_rounds rounds of those tiles, the idle share of
+    // their CU-rounds times K reaches 320, from K = 950 on.
+    auto psk_pays = [&](int64_t max_rounds) {
+        const int64_t t = tiles(kCfgDma64x64K32), r = ceil_div(t, CU);
+        return K >= 950 && t <= max_rounds * CU && (r * CU - t) * K >= 320 * r * CU;
+    };
     // A side of at most 64 (or 129 to 192) leaves 128-wide tiles a half (a
     // third) padding; once their padded area is over a quarter larger than
     // that of 64 x 64 tiles, only the 64 x 64 choices below are taken
@@ -1913,7 +1920,9 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
             return deep_ok ? kCfgDma128x128K64PSK : kCfgDma128x128K32W16SK;
         if (K >= 1024 && t128 <= 2 * CU && !unbalanced(kCfgDma128x128K64P))
             return kCfgDma128x128K32P;
-        return kCfgDma64x64K32;
+        // (Up to six rounds of 64 x 64 tiles, stream-K over the 8 pipelined
+        // groups where it pays: 198 x 16642 x 1898: 149.5 us against 166.7.)
+        return psk_pays(6) ? kCfgDma64x64K16S8PSK : kCfgDma64x64K32;
     }
     // At least three quarters of the CUs busy with 128 x 128 tiles: one
     // round of them where 64 x 64 tiles would take four rounds, as much
@@ -2031,9 +2040,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 1137: 40.6 against 43.7; on 10 random shapes of 257-320 64 x 64 tiles
     // with K in 513-950: 0.1 % above the per-shape best, against 10 % for
     // stream-K; but 1993 x 539 x 1078: 39.8 against 39.4).
-    const int64_t rounds = ceil_div(t32, CU);
-    if (K >= 950 && t32 <= 3 * CU && (rounds * CU - t32) * K >= 320 * rounds * CU &&
-        (t32 > 5 * CU / 4 || K >= 1536))
+    if (psk_pays(6) && (t32 > 5 * CU / 4 || K >= 1536))
         return kCfgDma64x64K16S8PSK;
     if (K > 512 && t32 <= 5 * CU / 4)
         return K < 1150 ? kCfgDma32x32K32S4 : kCfgDma64x64K32S4SK;
