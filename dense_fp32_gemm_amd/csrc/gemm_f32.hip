@@ -1858,9 +1858,12 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // Stream-K over the 8 pipelined groups of 64 x 64 tiles (below) pays
     // where, with up to max_rounds rounds of those tiles, the idle share of
     // their CU-rounds times K reaches 320, from K = 950 on.
-    auto psk_pays = [&](int64_t max_rounds) {
+    auto idle_k = [&]() {   // idle share of the CU-rounds of 64 x 64 tiles, times K
         const int64_t t = tiles(kCfgDma64x64K32), r = ceil_div(t, CU);
-        return K >= 950 && t <= max_rounds * CU && (r * CU - t) * K >= 320 * r * CU;
+        return (r * CU - t) * K / (r * CU);
+    };
+    auto psk_pays = [&](int64_t max_rounds) {
+        return K >= 950 && tiles(kCfgDma64x64K32) <= max_rounds * CU && idle_k() >= 320;
     };
     // A side of at most 64 (or 129 to 192) leaves 128-wide tiles a half (a
     // third) padding; once their padded area is over a quarter larger than
@@ -1931,11 +1934,19 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 211 against 235; 3394 x 1064 x 960, 918 64 x 64 tiles: 62.9 against
     // 69.5; but 3072 x 1024 x 2048, 192 (768): 126 against 109; 1551 x 1838
     // x 1619, 195 (725): 104.6 against 88.3); the loader-wave tile's 64-deep
-    // panels unless the last one would be at most half used, then 32-deep
-    // ones (2286 x 1396 x 758: 53.6 us against 54.0; 2282 x 1391 x 771: 57.6
-    // against 60.1).
-    if (!thin && K > 512 && 4 * t128 >= 3 * CU && ceil_div(tiles(kCfgDma64x64K32), CU) >= 4)
-        return deep_ok && 64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) ? kCfgDma128x128K64P : kCfgDma128x128K32P;
+    // panels unless the last one would be at most half used and its padding
+    // over 1/32 of K, then 32-deep ones (2286 x 1396 x 758: 53.6 us against
+    // 54.0; 2282 x 1391 x 771: 57.6 against 60.1; but 1800 x 1800 x 2500:
+    // 152.9 against 155.2 for 32-deep panels).  Not where the fourth round of 64 x 64 tiles is nearly
+    // empty and K long, idle share x K >= 1000: stream-K over the 8
+    // pipelined groups then does less (1664 x 1950 x 11185: 603 us against
+    // 636; 1700 x 1900 x 5000: 276 against 292; but 2000 x 1700 x 4000,
+    // 625: 237.6 against 234.6).
+    if (!thin && K > 512 && 4 * t128 >= 3 * CU && ceil_div(tiles(kCfgDma64x64K32), CU) >= 4 &&
+        !(psk_pays(6) && idle_k() >= 1000))
+        return deep_ok && (64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) || 32 * (64 * ceil_div(K, 64) - K) <= K)
+                   ? kCfgDma128x128K64P
+                   : kCfgDma128x128K32P;
     // 64 x 64 tiles with K > 512 (one round: K >= 400), up to three rounds
     // of them.  One tile per CU: 8 pipelined one-wave K-split groups from K
     // = 640 on (and from 400 to 512), unless the

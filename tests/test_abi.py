@@ -288,6 +288,10 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # round of 128 x 128, 32-deep panels if a 64-deep last one would be at
     # most half used; three rounds of 64 x 64 tiles: those
     ((3394, 1064, 960), "dma_128x128x64_pipe_lw2 "), ((2282, 1391, 771), "dma_128x128x32_pipe "),
+    ((1800, 1800, 2500), "dma_128x128x64_pipe_lw2 "), ((2000, 1700, 4000), "dma_128x128x64_pipe_lw2 "),
+    # unless the fourth round of 64 x 64 tiles is nearly empty and K long:
+    # stream-K over the 8 pipelined groups
+    ((1664, 1950, 11185), "dma_64x64x16_ksplit8_pipe_sk "), ((1700, 1900, 5000), "dma_64x64x16_ksplit8_pipe_sk "),
     ((1551, 1838, 1619), "dma_64x64x32 "), ((3072, 1024, 2048), "dma_64x64x16_ksplit8_pipe "),
     # 486 128 x 128 tiles (a second round 90 % full) with 1024 <= K < 2048:
     # two rounds of the 32-deep pipelined tile; 324 (27 % full): 64 x 64
