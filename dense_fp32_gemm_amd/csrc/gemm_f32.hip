@@ -1857,13 +1857,14 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     };
     // Stream-K over the 8 pipelined groups of 64 x 64 tiles (below) pays
     // where, with up to max_rounds rounds of those tiles, the idle share of
-    // their CU-rounds times K reaches 320, from K = 950 on.
+    // their CU-rounds times K reaches min_idle_k (320 against the whole-tile
+    // choices of the 64 x 64 region), from K = 950 on.
     auto idle_k = [&]() {   // idle share of the CU-rounds of 64 x 64 tiles, times K
         const int64_t t = tiles(kCfgDma64x64K32), r = ceil_div(t, CU);
         return (r * CU - t) * K / (r * CU);
     };
-    auto psk_pays = [&](int64_t max_rounds) {
-        return K >= 950 && tiles(kCfgDma64x64K32) <= max_rounds * CU && idle_k() >= 320;
+    auto psk_pays = [&](int64_t max_rounds, int64_t min_idle_k) {
+        return K >= 950 && tiles(kCfgDma64x64K32) <= max_rounds * CU && idle_k() >= min_idle_k;
     };
     // A side of at most 64 (or 129 to 192) leaves 128-wide tiles a half (a
     // third) padding; once their padded area is over a quarter larger than
@@ -1924,8 +1925,12 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         if (K >= 1024 && t128 <= 2 * CU && !unbalanced(kCfgDma128x128K64P))
             return kCfgDma128x128K32P;
         // (Up to six rounds of 64 x 64 tiles, stream-K over the 8 pipelined
-        // groups where it pays: 198 x 16642 x 1898: 149.5 us against 166.7.)
-        return psk_pays(6) ? kCfgDma64x64K16S8PSK : kCfgDma64x64K32;
+        // groups where it pays, here from an idle share x K of 160 on, the
+        // 64 x 64 tiles of 4 waves being the alternative: 198 x 16642 x
+        // 1898: 149.5 us against 166.7; 2600 x 2000 x 1800: 169.5 against
+        // 184.3; 3317 x 1235 x 1323: 111.1 against 118.7; but 1500 x 3500 x
+        // 1050, 148: 119.2 against 110.3.)
+        return psk_pays(6, 160) ? kCfgDma64x64K16S8PSK : kCfgDma64x64K32;
     }
     // At least three quarters of the CUs busy with 128 x 128 tiles: one
     // round of them where 64 x 64 tiles would take four rounds, as much
@@ -1943,7 +1948,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 636; 1700 x 1900 x 5000: 276 against 292; but 2000 x 1700 x 4000,
     // 625: 237.6 against 234.6).
     if (!thin && K > 512 && 4 * t128 >= 3 * CU && ceil_div(tiles(kCfgDma64x64K32), CU) >= 4 &&
-        !(psk_pays(6) && idle_k() >= 1000))
+        !psk_pays(6, 1000))
         return deep_ok && (64 * ceil_div(K, 64) == 32 * ceil_div(K, 32) || 32 * (64 * ceil_div(K, 64) - K) <= K)
                    ? kCfgDma128x128K64P
                    : kCfgDma128x128K32P;
@@ -2051,7 +2056,7 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
     // 1137: 40.6 against 43.7; on 10 random shapes of 257-320 64 x 64 tiles
     // with K in 513-950: 0.1 % above the per-shape best, against 10 % for
     // stream-K; but 1993 x 539 x 1078: 39.8 against 39.4).
-    if (psk_pays(6) && (t32 > 5 * CU / 4 || K >= 1536))
+    if (psk_pays(6, 320) && (t32 > 5 * CU / 4 || K >= 1536))
         return kCfgDma64x64K16S8PSK;
     if (K > 512 && t32 <= 5 * CU / 4)
         return K < 1150 ? kCfgDma32x32K32S4 : kCfgDma64x64K32S4SK;

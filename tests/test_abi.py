@@ -279,7 +279,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # four to six rounds of 64 x 64 tiles where the 128 x 128 choices do not
     # apply: stream-K over the 8 pipelined groups where it pays
     ((198, 16642, 1898), "dma_64x64x16_ksplit8_pipe_sk "), ((29205, 160, 3003), "dma_64x64x16_ksplit8_pipe_sk "),
-    ((42104, 99, 1696), "dma_64x64x32 "),
+    ((42104, 99, 1696), "dma_64x64x16_ksplit8_pipe_sk "), ((1500, 3500, 1050), "dma_64x64x32 "),
     # just past one round of 64 x 64 tiles with K < 1150: 32 x 32 tiles of 4
     # K-split groups
     ((309, 3485, 597), "dma_32x32x32_ksplit4 "), ((660, 1684, 979), "dma_32x32x32_ksplit4 "),
