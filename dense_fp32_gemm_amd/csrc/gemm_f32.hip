@@ -2071,8 +2071,13 @@ int select_config(int M, int N, int K, bool dma_ok, bool deep_ok, int64_t CU, in
         return kCfgDma64x64K16S8P;
     if (K >= 2048 && t32 <= 3 * CU)
         return kCfgDma64x64K16S8P;
+    // 64 x 128 (128 x 64) tiles with at least two per CU, unless a side
+    // pads 128-wide tiles a quarter more (48857 x 138 x 860: 146.6 us
+    // against 137.0 for 64 x 64 tiles; 33933 x 157 x 708: 104.3 against
+    // 92.0; but 64 x 65536 x 1024, exactly two rounds of 64 x 128 tiles:
+    // 74.8 against 74.3).
     const int wide = N >= M ? kCfgDma64x128K32 : kCfgDma128x64K32;
-    if (tiles(wide) >= 2 * CU)
+    if (!thin && tiles(wide) >= 2 * CU)
         return wide;
     // 64 x 64 tiles.  Up to two per CU, the one or two 4-wave workgroups
     // leave each SIMD one or two waves, and 64-deep panels halve the

@@ -257,7 +257,7 @@ def test_wide_rows_fall_back_to_staged_kernels():
     # padding, so only the 64 x 64 choices; a side of 96 or 128 keeps them
     ((64, 32768, 4096), "dma_64x64x16_ksplit8_pipe "), ((32768, 64, 4096), "dma_64x64x16_ksplit8_pipe "),
     ((192, 16384, 4096), "dma_64x64x16_ksplit8_pipe "), ((64, 32768, 1024), "dma_64x64x16_ksplit8_pipe "),
-    ((64, 65536, 1024), "dma_64x128x32 "), ((65536, 64, 1024), "dma_128x64x32 "),
+    ((64, 65536, 1024), "dma_64x64x32 "), ((65536, 64, 1024), "dma_64x64x32 "),
     ((96, 32768, 4096), "dma_128x128x64_pipe_lw2 "), ((128, 32768, 4096), "dma_128x128x64_pipe_lw2 "),
     # a second round exactly half full (384 tiles): stream-K over the 8
     # pipelined groups
